@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for the attention forward (bf16 bit patterns).
+
+The arrays this module returns feed both the HIP library and the fp64 oracle;
+it holds none of the attention arithmetic. The generator itself is C
+(``gen.c``, built into ``liblsvgen.so``), counter-based, so results do not
+depend on the number of threads. See ``gen.c`` for the exact definitions.
+
+Workloads stand in for the MiniMax-H3 packed clips the pages describe
+(TensorRT-LLM PR #21275, Description and Measurements: 19k / 38k / 104k-token
+blocks with 56 heads x 128; the 544x960x124 clip packs to 19,394 tokens;
+FastVideo perf/ulysses-h3-adaptive commit message: sp=4 gives one rank 14 of
+the 56 heads). Tensor ids: Q = 0, K = 1, V = 2, boosted-K row choice = 3.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblsvgen.so")
+SOURCE_PATH = os.path.join(_HERE, "gen.c")
+
+Q_ID, K_ID, V_ID, CHOOSE_ID = 0, 1, 2, 3
+RMS_EPS = 1e-5  # the H3 QK-norm eps (FastVideo #2049, MotionKernel qkv prologue)
+
+_lib = None
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile ``gen.c`` with gcc into ``liblsvgen.so`` (always recompiles)."""
+    import subprocess
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11",
+           SOURCE_PATH, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build_library()
+    lib = ctypes.CDLL(LIB_PATH)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.lsvgen_normal_bf16.argtypes = [u16p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32]
+    lib.lsvgen_rms_normalize_bf16.argtypes = [u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
+    lib.lsvgen_choose.argtypes = [i64p, ctypes.c_int64, ctypes.c_int64, i64p, ctypes.c_uint64, ctypes.c_uint32]
+    lib.lsvgen_scale_rows_bf16.argtypes = [u16p, i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float]
+    lib.lsvgen_normal_f64_at.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64]
+    lib.lsvgen_normal_f64_at.restype = ctypes.c_double
+    for f in (lib.lsvgen_normal_bf16, lib.lsvgen_rms_normalize_bf16, lib.lsvgen_choose,
+              lib.lsvgen_scale_rows_bf16):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"{what}: invalid arguments")
+
+
+def normal_bf16(n: int, seed: int, tensor: int) -> np.ndarray:
+    """``n`` bf16 standard normals (uint16 bit patterns) of stream (seed, tensor)."""
+    out = np.empty(n, dtype=np.uint16)
+    lib = _load()
+    _check(lib.lsvgen_normal_bf16(out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), n, seed, tensor),
+           "normal_bf16")
+    return out
+
+
+def normal_f64_at(seed: int, tensor: int, e: int) -> float:
+    """Element ``e`` of stream (seed, tensor) before rounding (for tests)."""
+    return _load().lsvgen_normal_f64_at(seed, tensor, e)
+
+
+def rms_normalize_rows(x: np.ndarray, eps: float = RMS_EPS) -> None:
+    """In place: every last-axis row ``x <- bf16(x * (mean(x^2) + eps)^-1/2)``."""
+    if x.dtype != np.uint16 or not x.flags.c_contiguous:
+        raise ValueError("expected a C-contiguous uint16 array")
+    d = x.shape[-1]
+    _check(_load().lsvgen_rms_normalize_bf16(x.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                             x.size // d, d, eps), "rms_normalize_rows")
+
+
+def choose_rows(n_choose: int, n_total: int, seed: int, tensor: int = CHOOSE_ID) -> np.ndarray:
+    """``n_choose`` distinct sorted indices in ``[0, n_total)`` (partial Fisher-Yates)."""
+    out = np.empty(n_choose, dtype=np.int64)
+    work = np.empty(max(n_total, 1), dtype=np.int64)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    _check(_load().lsvgen_choose(out.ctypes.data_as(i64p), n_choose, n_total, work.ctypes.data_as(i64p),
+                                 seed, tensor), "choose_rows")
+    return out
+
+
+def scale_rows(x: np.ndarray, rows: np.ndarray, factor: float) -> None:
+    """In place: multiply token rows ``rows`` of ``x`` ([T, ...], uint16 bf16) by ``factor``."""
+    if x.dtype != np.uint16 or not x.flags.c_contiguous:
+        raise ValueError("expected a C-contiguous uint16 array")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= x.shape[0]):
+        raise ValueError("row index out of range")
+    row_len = x.size // x.shape[0]
+    _check(_load().lsvgen_scale_rows_bf16(x.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                          rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                          rows.size, row_len, factor), "scale_rows")
+
+
+@dataclass
+class Inputs:
+    """One attention workload: packed bf16 q/k/v and its segment boundaries."""
+    name: str
+    q: np.ndarray           # uint16 [total, heads, head_dim]
+    k: np.ndarray
+    v: np.ndarray
+    cu_seqlens: np.ndarray  # int32 [n_seqs + 1]
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def n_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def seqlens(self) -> list[int]:
+        cu = self.cu_seqlens.astype(np.int64)
+        return [int(b - a) for a, b in zip(cu[:-1], cu[1:])]
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.seqlens, default=0)
+
+    def flops(self) -> float:
+        """Attention forward flops counted as sum over sequences of 4 * S^2 * H * D."""
+        return float(sum(4.0 * s * s * self.n_heads * self.head_dim for s in self.seqlens))
+
+
+def generate(seqlens, heads: int, head_dim: int = 128, *, seed: int, rms_qk: bool = False,
+             k_boost_frac: float = 0.0, k_boost_factor: float = 8.0, scale: float | None = None,
+             name: str = "custom", total_tokens: int | None = None) -> Inputs:
+    """Packed inputs for segments of lengths ``seqlens``.
+
+    * q, k, v: iid N(0,1) rounded to bf16, streams (seed, 0/1/2), row-major
+      ``[total, heads, head_dim]``.
+    * ``rms_qk``: every (token, head) row of q and k is RMS-normalised (unit
+      weight, eps 1e-5) in double and rounded to bf16.
+    * ``k_boost_frac``: ``round(frac * total)`` token rows of k, chosen by the
+      (seed, 3) stream, are multiplied by ``k_boost_factor`` on every head.
+    * ``scale`` defaults to ``1/sqrt(head_dim)``.
+    * ``total_tokens`` may exceed ``sum(seqlens)``; the extra rows are generated
+      too but lie outside every segment.
+    """
+    seqlens = [int(s) for s in seqlens]
+    if any(s < 0 for s in seqlens):
+        raise ValueError("negative sequence length")
+    used = sum(seqlens)
+    total = used if total_tokens is None else int(total_tokens)
+    if total < used:
+        raise ValueError("total_tokens smaller than the sum of seqlens")
+    shape = (total, heads, head_dim)
+    n = total * heads * head_dim
+    q = normal_bf16(n, seed, Q_ID).reshape(shape)
+    k = normal_bf16(n, seed, K_ID).reshape(shape)
+    v = normal_bf16(n, seed, V_ID).reshape(shape)
+    meta = {"seed": seed, "rms_qk": rms_qk, "k_boost_rows": 0}
+    if rms_qk:
+        rms_normalize_rows(q)
+        rms_normalize_rows(k)
+    if k_boost_frac > 0:
+        nb = int(round(k_boost_frac * total))
+        rows = choose_rows(nb, total, seed)
+        scale_rows(k, rows, k_boost_factor)
+        meta["k_boost_rows"] = nb
+        meta["k_boost_row_ids"] = rows
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    sc = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    return Inputs(name, q, k, v, cu, sc, meta)
+
+
+# The five workloads (tokens x heads x 128, bf16, seeds 1001..1005).
+CONFIGS = {
+    "tiny_s256_h4": dict(seqlens=[256], heads=4, seed=1001),
+    "s4096_h56_kboost": dict(seqlens=[4096], heads=56, seed=1002, k_boost_frac=0.01),
+    "sp4_share_s19394_h14": dict(seqlens=[19394], heads=14, seed=1003, rms_qk=True),
+    "h3_s38000_h56": dict(seqlens=[38000], heads=56, seed=1004, rms_qk=True),
+    "varlen_19394_38000_104000_h56": dict(seqlens=[19394, 38000, 104000], heads=56, seed=1005),
+}
+
+
+def make_config(name: str) -> Inputs:
+    """Inputs of one of the named workloads in ``CONFIGS``."""
+    if name not in CONFIGS:
+        raise KeyError(f"unknown workload {name!r}; known: {sorted(CONFIGS)}")
+    return generate(name=name, **CONFIGS[name])
