@@ -1,0 +1,81 @@
+/* lsv: dense non-causal varlen BF16 attention forward for AMD MI355X (gfx950).
+ *
+ * The operation (FastVideo #2049, diff of fastvideo/attention/utils/flash_attn_cute.py,
+ * the varlen forward wrapper; TensorRT-LLM PR #21275, Description): for every packed
+ * segment [a, b) = [cu_seqlens[s], cu_seqlens[s+1]), every head h and every query row
+ * i in [a, b),
+ *     z_ij     = scale * sum_d q[i,h,d] k[j,h,d]      (keys j of the same segment only)
+ *     O[i,h,:] = sum_j softmax_j(z_ij) v[j,h,:]
+ *     LSE[h,i] = ln sum_j exp(z_ij)
+ * Non-causal, no window, no softcap, one split (the forward is deterministic: the same
+ * inputs give bit-identical outputs on every run). The varlen test on the FastVideo
+ * #2049 page fixes the layouts: q/k/v/out are [total_tokens, heads, head_dim] and LSE
+ * is fp32 [heads, total_tokens]; one cu_seqlens vector serves queries and keys.
+ *
+ * All functions are plain C, return a status (0 = success, negative = error), never
+ * print, never throw, and never allocate device memory.
+ */
+#ifndef LSV_H
+#define LSV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lsv_status {
+  LSV_OK = 0,
+  LSV_ERR_INVALID_ARG = -1, /* null pointer, negative size, non-finite or non-positive scale */
+  LSV_ERR_UNSUPPORTED = -2, /* head_dim other than 128, or sizes beyond the launch limits */
+  LSV_ERR_ALIGNMENT = -3,   /* q/k/v/o not 16-byte aligned, lse/cu_seqlens not 4-byte aligned */
+  LSV_ERR_LAUNCH = -4,      /* the kernel launch failed (hipGetLastError after the launch) */
+  LSV_ERR_HIP = -5          /* another HIP runtime call failed (e.g. no device) */
+};
+
+/* Attention forward on the caller's stream (asynchronous; nothing is synchronised).
+ *
+ * q, k, v      device pointers, bf16 bit patterns, row-major [total_tokens, n_heads, head_dim],
+ *              16-byte aligned. Read only. Values are assumed finite.
+ * o            device pointer, bf16, same layout as q. Written for every token row that lies
+ *              inside a segment (rounded to nearest even from fp32); other rows untouched.
+ * lse          device pointer, fp32 [n_heads, total_tokens], natural log of the sum of
+ *              exp(scaled logits). Written for the same rows as o.
+ * cu_seqlens   device pointer, int32 [n_seqs + 1]: cu[0] = 0, non-decreasing,
+ *              cu[n_seqs] <= total_tokens, every cu[s+1] - cu[s] <= max_seqlen. It is never read
+ *              on the host. A segment that breaks the bounds (cu[s] < 0, cu[s+1] < cu[s] or
+ *              cu[s+1] > total_tokens) is skipped without any memory access outside [0,
+ *              total_tokens); rows of a segment longer than max_seqlen past the first
+ *              max_seqlen rounded up to 256 are not written.
+ * n_seqs       number of segments (>= 0). 0 is a successful no-op.
+ * max_seqlen   upper bound of the segment lengths (>= 0); sizes the grid. 0 is a no-op.
+ * total_tokens rows of q/k/v/o and columns of lse (>= 0).
+ * n_heads      >= 1.
+ * head_dim     must be 128.
+ * scale        softmax scale applied to q.k in fp32 (finite, > 0); e.g. 1/sqrt(128).
+ * stream       a hipStream_t, or NULL for the default stream.
+ *
+ * The caller owns every buffer; the library keeps no pointer after the call returns.
+ * Validation happens before any HIP call; on error nothing is launched.
+ */
+int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                 int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                 float scale, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* lsv_status_string(int status);
+
+/* Dense BF16 MFMA peak of `device` in TFLOP/s at its reported maximum clock:
+ * compute units x clock x 4096 flop per clock per compute unit (gfx950: one
+ * 32x32x16 bf16 MFMA, 32768 flop, per 32 clocks on each of 4 SIMDs).
+ * Writes *tflops and the CU count and clock (kHz) if the pointers are non-NULL. */
+int lsv_device_peak(int device, double* tflops, int* compute_units, int* clock_khz);
+
+/* Query-tile height (rows per workgroup) and key-tile width of the built kernel. */
+int lsv_tile_config(int* block_q, int* block_k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSV_H */

@@ -1,1 +1,146 @@
-"""lsv: dense non-causal varlen BF16 attention forward for MI355X (gfx950)."""
+"""lsv: dense non-causal varlen BF16 attention forward for MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in-tree by
+``python -m long_sequence_video_amd.build``). The functions named like the C entry points
+(``lsv_attn_fwd``, ``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only
+marshal arguments; ``attn_fwd`` adds torch-tensor conveniences (output allocation, the
+current stream). There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_status_string", "lsv_device_peak",
+    "lsv_tile_config", "attn_fwd", "flops", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
+EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_status_string", "lsv_device_peak", "lsv_tile_config")
+
+LSV_OK = 0
+LSV_ERR_INVALID_ARG = -1
+LSV_ERR_UNSUPPORTED = -2
+LSV_ERR_ALIGNMENT = -3
+LSV_ERR_LAUNCH = -4
+LSV_ERR_HIP = -5
+
+_lib = None
+
+
+class LsvError(ValueError):
+    """A negative status returned by the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lsv_status_string(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load ``liblsv.so`` (once) and declare the C signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m long_sequence_video_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.lsv_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, vp]
+    lib.lsv_attn_fwd.restype = ctypes.c_int
+    lib.lsv_status_string.argtypes = [ctypes.c_int]
+    lib.lsv_status_string.restype = ctypes.c_char_p
+    lib.lsv_device_peak.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
+                                    ctypes.POINTER(ctypes.c_int)]
+    lib.lsv_device_peak.restype = ctypes.c_int
+    lib.lsv_tile_config.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    lib.lsv_tile_config.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def lsv_attn_fwd(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, n_seqs: int, max_seqlen: int,
+                 total_tokens: int, n_heads: int, head_dim: int, scale: float, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_fwd(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads,
+                                       head_dim, scale, stream)
+
+
+def lsv_status_string(status: int) -> str:
+    return load_library().lsv_status_string(status).decode()
+
+
+def lsv_device_peak(device: int = 0) -> tuple[float, int, int]:
+    """(dense BF16 MFMA TFLOP/s at the reported max clock, compute units, clock kHz)."""
+    tf, cus, khz = ctypes.c_double(), ctypes.c_int(), ctypes.c_int()
+    rc = load_library().lsv_device_peak(device, ctypes.byref(tf), ctypes.byref(cus), ctypes.byref(khz))
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_device_peak")
+    return tf.value, cus.value, khz.value
+
+
+def lsv_tile_config() -> tuple[int, int]:
+    """(query rows per workgroup, keys per tile) of the built kernel."""
+    bq, bk = ctypes.c_int(), ctypes.c_int()
+    load_library().lsv_tile_config(ctypes.byref(bq), ctypes.byref(bk))
+    return bq.value, bk.value
+
+
+def flops(seqlens, n_heads: int, head_dim: int = 128) -> float:
+    """Attention forward flops counted as sum over sequences of 4 * S^2 * H * D."""
+    return float(sum(4.0 * s * s * n_heads * head_dim for s in seqlens))
+
+
+def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | None = None, *, out=None,
+             lse=None, stream=None):
+    """Attention forward on torch tensors (all on one GPU).
+
+    Args:
+      q, k, v: bfloat16 ``[total_tokens, n_heads, 128]``, contiguous.
+      cu_seqlens: int32 ``[n_seqs + 1]`` on the same device.
+      max_seqlen: largest segment length; computed from ``cu_seqlens`` (a device-to-host
+        copy) when omitted.
+      scale: softmax scale; default ``1 / sqrt(head_dim)``.
+      out, lse: optional preallocated outputs (``[T, H, D]`` bf16, ``[H, T]`` fp32).
+      stream: a ``torch.cuda.Stream``; default: the current stream.
+
+    Returns:
+      ``(out, lse)``.
+    """
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [total_tokens, heads, head_dim] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in (k, v, cu_seqlens)):
+        raise ValueError("all tensors must be on the same GPU")
+    total, heads, dim = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, max_seqlen, total, heads, dim, scale,
+                          s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_fwd")
+    return out, lse

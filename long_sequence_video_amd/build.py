@@ -1,0 +1,68 @@
+"""Build the native libraries in-tree.
+
+* ``liblsv.so``  — the HIP attention library (C ABI in ``include/lsv.h``), gfx950 only.
+* ``inputs/liblsvgen.so`` — the seeded input generator (plain C, OpenMP).
+
+Run ``python -m long_sequence_video_amd.build``. Every call recompiles.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+HIP_SOURCE = os.path.join(PKG, "csrc", "attn_fwd.hip")
+HIP_LIB = os.path.join(PKG, "liblsv.so")
+INCLUDE = os.path.join(ROOT, "include")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the attention library)")
+
+
+def hip_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # inputs are finite by contract; lets fmaxf lower to v_max3 without NaN canonicalisation
+        "-fno-honor-nans",
+        # MFMA accumulators in VGPRs (the softmax reads the score accumulator on the VALU)
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+        # no packed-fp32 instructions (v_pk_*_f32) in generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE,
+    ]
+
+
+def build_hip(verbose: bool = False) -> str:
+    tmp = HIP_LIB + ".tmp"
+    cmd = [hipcc(), *hip_flags(), HIP_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, HIP_LIB)
+    return HIP_LIB
+
+
+def build(verbose: bool = False) -> None:
+    """Compile every native part of the package (always recompiles)."""
+    from .inputs import build_library
+    build_library(verbose=verbose)
+    build_hip(verbose=verbose)
+
+
+if __name__ == "__main__":
+    build(verbose=True)

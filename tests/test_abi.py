@@ -1,0 +1,83 @@
+"""The C-ABI library: it loads, exports every declared symbol, and validates arguments on the
+host before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_sequence_video_amd as lsv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(lsv.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(lsv.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert lsv.lsv_status_string(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert lsv.lsv_status_string(code) not in ("ok", "unknown status")
+    assert lsv.lsv_status_string(-99) == "unknown status"
+
+
+def test_tile_config():
+    bq, bk = lsv.lsv_tile_config()
+    assert bq > 0 and bk > 0 and bq % 32 == 0 and bk % 32 == 0
+
+
+# Fake, suitably aligned addresses: validation must reject before touching them.
+A = 1 << 20
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(head_dim=8), lsv.LSV_ERR_UNSUPPORTED),          # the pages' q [7, 2, 8] example
+    (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_seqs=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(max_seqlen=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(total_tokens=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=-0.1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(q=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(lse=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(cu=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(v=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(o=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(lse=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(total_tokens=1 << 31), lsv.LSV_ERR_UNSUPPORTED),
+    # successful no-ops: nothing to compute, nothing launched
+    (dict(n_seqs=0), lsv.LSV_OK),
+    (dict(max_seqlen=0), lsv.LSV_OK),
+    (dict(total_tokens=0), lsv.LSV_OK),
+    (dict(n_seqs=0, q=0, k=0, v=0, o=0, lse=0, cu=0), lsv.LSV_OK),
+])
+def test_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, n_seqs=1, max_seqlen=10, total_tokens=10, n_heads=4, head_dim=128,
+             scale=0.125)
+    a.update(args)
+    rc = lsv.lsv_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["n_seqs"], a["max_seqlen"],
+                          a["total_tokens"], a["n_heads"], a["head_dim"], a["scale"], None)
+    assert rc == code
+
+
+def test_flops_count():
+    assert lsv.flops([19394, 38000, 104000], 56) == 4 * (19394 ** 2 + 38000 ** 2 + 104000 ** 2) * 56 * 128
+    assert lsv.flops([104000], 56) == 4 * 104000 ** 2 * 56 * 128

@@ -1,0 +1,195 @@
+"""GPU parity of the HIP attention forward against the fp64 oracle, through the C ABI.
+
+Tolerances (bf16 output vs unrounded fp64 O: max-abs 2e-2, mean-abs 2e-3; fp32 LSE:
+max-abs 1e-3). Small cases are checked on every row; the full-size workloads, run in the
+same launch configuration the benchmark times, are checked on sampled rows (the first and
+last query tile of each segment plus random rows), plus bit-exact properties that hold at
+any size (determinism, segment isolation).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from long_sequence_video_amd import inputs as gen
+from oracle import bf16_bits_to_f64
+from tests.gpu_common import compare, run_kernel, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- small, every row
+
+def test_tiny_config_all_rows(gpu):
+    inp = gen.make_config("tiny_s256_h4")
+    say("case tiny_s256_h4")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, label="tiny_s256_h4")
+
+
+@pytest.mark.parametrize("seqlens,heads", [
+    ([1], 1),
+    ([31], 2),
+    ([32], 2),
+    ([33], 2),
+    ([127, 128, 129], 3),
+    ([255, 256, 257], 2),
+    ([1, 0, 5, 0, 300, 2, 64], 3),
+    ([1000], 4),
+    ([200, 1700, 37], 2),
+])
+def test_ragged_varlen_all_rows(gpu, seqlens, heads):
+    inp = gen.generate(seqlens, heads, seed=77 + len(seqlens) + heads, name="ragged")
+    say(f"case ragged {seqlens} h{heads}")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, label=f"ragged {seqlens} h{heads}")
+
+
+def test_scale_values(gpu):
+    for scale in (0.125, 0.02, 0.3):
+        inp = gen.generate([300, 77], 2, seed=5, scale=scale, name="scale")
+        say(f"case scale {scale}")
+        out, lse = run_kernel(inp, gpu)
+        compare(inp, out, lse, label=f"scale {scale}")
+
+
+def test_rows_outside_segments_untouched_and_poison_ignored(gpu):
+    """Tokens past cu[-1] hold NaN in q/k/v; outputs there keep their sentinel, and the
+    segments' outputs are finite and match the oracle."""
+    inp = gen.generate([100, 0, 61], 2, seed=11, total_tokens=200, name="poison")
+    for t in (inp.q, inp.k, inp.v):
+        t[161:] = 0x7FC0  # bf16 quiet NaN
+    say("case poison")
+    out, lse = run_kernel(inp, gpu, out_fill=0x1234, lse_fill=-7.0)
+    assert np.all(out[161:] == 0x1234)
+    assert np.all(lse[:, 161:] == -7.0)
+    compare(inp, out, lse, rows=np.arange(161), label="poison")
+
+
+def test_empty_inputs_are_noops(gpu):
+    import torch
+    import long_sequence_video_amd as lsv
+    say("case empty")
+    q = torch.zeros((8, 2, 128), dtype=torch.bfloat16, device=gpu)
+    out = torch.full_like(q, 3.0)
+    lse = torch.full((2, 8), 5.0, device=gpu)
+    cu = torch.tensor([0], dtype=torch.int32, device=gpu)
+    lsv.attn_fwd(q, q, q, cu, 0, 0.1, out=out, lse=lse)
+    cu = torch.tensor([0, 0, 0], dtype=torch.int32, device=gpu)
+    lsv.attn_fwd(q, q, q, cu, None, 0.1, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and bool((lse == 5.0).all())
+
+
+def test_unsupported_head_dim_raises(gpu):
+    """The pages' own interface example uses head_dim 8; this library supports 128 only."""
+    import torch
+    import long_sequence_video_amd as lsv
+    q = torch.zeros((7, 2, 8), dtype=torch.bfloat16, device=gpu)
+    cu = torch.tensor([0, 7], dtype=torch.int32, device=gpu)
+    with pytest.raises(lsv.LsvError) as e:
+        lsv.attn_fwd(q, q, q, cu, 7, 0.125)
+    assert e.value.status == lsv.LSV_ERR_UNSUPPORTED
+    q = torch.randn((7, 2, 128), device=gpu).to(torch.bfloat16)
+    out, lse = lsv.attn_fwd(q, q, q, cu, 7, 0.125)
+    assert list(out.shape) == [7, 2, 128] and list(lse.shape) == [2, 7]
+
+
+# ---------------------------------------------------------------- closed forms on the GPU
+
+def test_dominant_logit_gives_exact_value_row(gpu):
+    """Key j* = bf16(8 q_i) sits in a late tile after smaller maxima: O_i equals V[j*]
+    bit for bit (p* = 1 after the max is raised, the rest underflow)."""
+    L, H = 1000, 2
+    inp = gen.generate([L], H, seed=3, name="dominant")
+    k = inp.k
+    i, jstar = 17, 900
+    for h in range(H):
+        qf = bf16_bits_to_f64(inp.q[i, h])
+        k[jstar, h] = (np.float32(8.0) * qf.astype(np.float32)).view(np.uint32).astype(np.uint64).__rshift__(16).astype(np.uint16)
+    say("case dominant logit")
+    out, lse = run_kernel(inp, gpu)
+    assert np.array_equal(out[i], inp.v[jstar]), (out[i][:, :8], inp.v[jstar][:, :8])
+    compare(inp, out, lse, label="dominant")
+
+
+def test_identical_keys_mean_of_values(gpu):
+    L, H = 700, 2
+    inp = gen.generate([L], H, seed=4, name="identical")
+    inp.k[:] = inp.k[5]
+    say("case identical keys")
+    out, lse = run_kernel(inp, gpu)
+    vmean = bf16_bits_to_f64(inp.v).mean(axis=0)
+    got = bf16_bits_to_f64(out)
+    assert np.abs(got - vmean[None]).max() < 2e-2
+    compare(inp, out, lse, label="identical")
+
+
+def test_key_value_permutation_within_tolerance(gpu):
+    inp = gen.generate([513], 2, seed=6, name="perm")
+    say("case permutation")
+    out1, lse1 = run_kernel(inp, gpu)
+    perm = np.random.default_rng(0).permutation(513)
+    inp.k[:] = inp.k[perm]
+    inp.v[:] = inp.v[perm]
+    out2, lse2 = run_kernel(inp, gpu)
+    d = np.abs(bf16_bits_to_f64(out1) - bf16_bits_to_f64(out2))
+    assert d.max() <= 2 * 2e-2 and np.abs(lse1 - lse2).max() <= 2e-3
+    compare(inp, out2, lse2, label="perm")
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+_cache = {}
+
+
+def _config(name):
+    if name not in _cache:
+        _cache.clear()
+        _cache[name] = gen.make_config(name)
+    return _cache[name]
+
+
+def test_c2_boosted_keys(gpu):
+    inp = _config("s4096_h56_kboost")
+    say("case s4096_h56_kboost")
+    out, lse = run_kernel(inp, gpu)
+    rows = sample_rows(inp, 384, seed=2)
+    compare(inp, out, lse, rows=rows, label="s4096_h56_kboost")
+    # every row is finite
+    assert np.isfinite(bf16_bits_to_f64(out)).all() and np.isfinite(lse).all()
+
+
+def test_c3_sp4_share(gpu):
+    inp = _config("sp4_share_s19394_h14")
+    say("case sp4_share_s19394_h14")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, rows=sample_rows(inp, 256, seed=3), label="sp4_share_s19394_h14")
+
+
+def test_c4_h3_38000(gpu):
+    inp = _config("h3_s38000_h56")
+    say("case h3_s38000_h56")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, rows=sample_rows(inp, 64, seed=4), label="h3_s38000_h56")
+
+
+def test_c5_varlen_and_segment_isolation(gpu):
+    import torch
+    inp = _config("varlen_19394_38000_104000_h56")
+    say("case varlen_19394_38000_104000_h56")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, rows=sample_rows(inp, 32, seed=5), label="varlen_161394_h56")
+    # run-to-run determinism: bit-identical
+    say("case varlen determinism")
+    out2, lse2 = run_kernel(inp, gpu)
+    assert np.array_equal(out, out2) and np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
+    del out2, lse2
+    # the 104k segment run alone equals the same rows inside the pack, bit for bit
+    say("case 104k alone")
+    a, b = int(inp.cu_seqlens[2]), int(inp.cu_seqlens[3])
+    alone = gen.Inputs("c5_104k", inp.q[a:b], inp.k[a:b], inp.v[a:b], np.array([0, b - a], np.int32), inp.scale)
+    out3, lse3 = run_kernel(alone, gpu)
+    assert np.array_equal(out3, out[a:b]) and np.array_equal(lse3.view(np.uint32), lse[:, a:b].view(np.uint32))
+    torch.cuda.empty_cache()
