@@ -6,11 +6,17 @@ clips, 19,394 + 38,000 + 104,000 tokens x 56 heads x 128 (161,394 tokens; 3.623e
 per step). Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+  python bench.py --copy-bytes N   # a plain device copy of N bytes, to calibrate HBM counters
+
+roofline.traffic (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+summary committed under profiles/ for this workload, scaled by the same counters on a copy of
+known size; it is null when that summary was taken on a different kernel source.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -26,6 +32,46 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense BF16 MFMA peak (2.5 PFLOP/s)
 DEFAULT_CONFIG = "varlen_19394_38000_104000_h56"
 # The segment of the default pack that the 40% target is stated for, run alone.
 EXTRA_CONFIGS = {"h56_s104000": dict(seqlens=[104000], heads=56, seed=1005)}
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "long_sequence_video_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_{workload}_hbm_traffic.md")
+
+
+def kernel_source_sha256() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """(bytes per launch, summary path) from the committed counter summary, if it was taken
+    on the current kernel source; else (None, reason)."""
+    path = TRAFFIC_SUMMARY.format(workload=workload)
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+        return None, "counter summary predates the current kernel source"
+    try:
+        return float(fields["hbm_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    except (KeyError, ValueError):
+        return None, "counter summary lacks hbm_bytes_per_launch"
+
+
+def copy_calibration(nbytes: int, steps: int):
+    """A plain device-to-device copy of nbytes, repeated: the reference kernel for the HBM
+    counters (it reads and writes exactly nbytes per launch)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_bytes": nbytes, "launches": steps}), flush=True)
 
 
 def log(*a):
@@ -60,15 +106,18 @@ def cpu_baseline(inp, target_seconds: float = 15.0):
             f += 4.0 * n * (b - a) * inp.n_heads * inp.head_dim
         return f
 
-    # calibrate on a small sample, then size the timed sample to ~target_seconds
-    rows = sample(4)
-    t0 = time.perf_counter()
-    attention_fp64(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.scale, rows=rows, workers=cores)
-    dt = time.perf_counter() - t0
-    rate = flops_of(rows) / max(dt, 1e-6)
-    per_seg = 4
-    while per_seg < 4096 and flops_of(sample(per_seg * 2)) / rate < target_seconds:
-        per_seg *= 2
+    # calibrate on a sample of ~1 s, then size the timed sample to ~target_seconds
+    per_seg = 16
+    while True:
+        rows = sample(per_seg)
+        t0 = time.perf_counter()
+        attention_fp64(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.scale, rows=rows, workers=cores)
+        dt = time.perf_counter() - t0
+        if dt > 1.0 or per_seg >= 4096:
+            break
+        per_seg *= 4
+    rate = flops_of(rows) / dt
+    per_seg = max(1, min(8192, int(per_seg * target_seconds * rate / max(flops_of(rows), 1.0))))
     rows = sample(per_seg)
     t0 = time.perf_counter()
     attention_fp64(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.scale, rows=rows, workers=cores)
@@ -92,6 +141,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="run the counter-calibration copy instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward of one rank's share runs on a "
@@ -99,6 +149,10 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+
+    if args.copy_bytes > 0:
+        copy_calibration(args.copy_bytes, args.steps)
+        return
 
     import torch
     import long_sequence_video_amd as lsv
@@ -137,6 +191,9 @@ def main():
     log(f"{args.config}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s, {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
 
     peak_at_clock, cus, khz = lsv.lsv_device_peak(0)
+    traffic, traffic_src = measured_traffic(inp.name)
+    # HBM-minimal bytes per launch: q, k, v read once, O written once (bf16), LSE (fp32).
+    algorithmic_bytes = 4 * inp.total_tokens * inp.n_heads * inp.head_dim * 2 + inp.total_tokens * inp.n_heads * 4
     result = {
         "metric": "BF16 attn fwd TFLOP/s (4*S^2*H*D), 56h x 128d, 19k-104k tok; % MFMA peak",
         "value": round(tflops, 2),
@@ -167,7 +224,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch",
+            "traffic_source": traffic_src,
+            "algorithmic_hbm_bytes": algorithmic_bytes,
             "kernel": "attn_fwd_kernel",
             "peak_at_reported_clock": round(peak_at_clock, 1),
             "compute_units": cus,

@@ -44,11 +44,13 @@ enum lsv_status {
  * cu_seqlens   device pointer, int32 [n_seqs + 1]: cu[0] = 0, non-decreasing,
  *              cu[n_seqs] <= total_tokens, every cu[s+1] - cu[s] <= max_seqlen. It is never read
  *              on the host. A segment that breaks the bounds (cu[s] < 0, cu[s+1] < cu[s] or
- *              cu[s+1] > total_tokens) is skipped without any memory access outside [0,
- *              total_tokens); rows of a segment longer than max_seqlen past the first
- *              max_seqlen rounded up to 256 are not written.
+ *              cu[s+1] > total_tokens) or is longer than max_seqlen is skipped: none of its
+ *              rows is written and nothing outside [0, total_tokens) is read.
  * n_seqs       number of segments (>= 0). 0 is a successful no-op.
  * max_seqlen   upper bound of the segment lengths (>= 0); sizes the grid. 0 is a no-op.
+ *              The kernel addresses one head's K/V rows of a segment with 32-bit byte
+ *              offsets: max_seqlen * n_heads * head_dim * 2 must stay below 2^32 (e.g.
+ *              max_seqlen <= 299,593 at 56 heads), else LSV_ERR_UNSUPPORTED.
  * total_tokens rows of q/k/v/o and columns of lse (>= 0).
  * n_heads      >= 1.
  * head_dim     must be 128.

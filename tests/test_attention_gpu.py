@@ -7,8 +7,6 @@ last query tile of each segment plus random rows), plus bit-exact properties tha
 any size (determinism, segment isolation).
 """
 
-import math
-
 import numpy as np
 import pytest
 
@@ -17,6 +15,13 @@ from oracle import bf16_bits_to_f64
 from tests.gpu_common import compare, run_kernel, sample_rows, say
 
 pytestmark = pytest.mark.gpu
+
+
+def _bits(x):
+    """float -> bf16 bits (via float32, round to nearest even)."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
 # ---------------------------------------------------------------- small, every row
@@ -99,15 +104,15 @@ def test_unsupported_head_dim_raises(gpu):
 # ---------------------------------------------------------------- closed forms on the GPU
 
 def test_dominant_logit_gives_exact_value_row(gpu):
-    """Key j* = bf16(8 q_i) sits in a late tile after smaller maxima: O_i equals V[j*]
-    bit for bit (p* = 1 after the max is raised, the rest underflow)."""
+    """Key j* = bf16(8 q_i) sits in a late tile, ~127 log2 units above the first tile's
+    scores: O_i equals V[j*] bit for bit (its weight dominates every other by > 2^100)."""
     L, H = 1000, 2
     inp = gen.generate([L], H, seed=3, name="dominant")
     k = inp.k
     i, jstar = 17, 900
     for h in range(H):
         qf = bf16_bits_to_f64(inp.q[i, h])
-        k[jstar, h] = (np.float32(8.0) * qf.astype(np.float32)).view(np.uint32).astype(np.uint64).__rshift__(16).astype(np.uint16)
+        k[jstar, h] = _bits(8.0 * qf)  # exact: a power-of-two multiple of bf16 values
     say("case dominant logit")
     out, lse = run_kernel(inp, gpu)
     assert np.array_equal(out[i], inp.v[jstar]), (out[i][:, :8], inp.v[jstar][:, :8])
@@ -193,3 +198,47 @@ def test_c5_varlen_and_segment_isolation(gpu):
     out3, lse3 = run_kernel(alone, gpu)
     assert np.array_equal(out3, out[a:b]) and np.array_equal(lse3.view(np.uint32), lse[:, a:b].view(np.uint32))
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- dynamic range (exact fallback)
+
+
+def test_overflowing_scores_take_exact_path(gpu):
+    """A late key 32 q_i scores ~500 log2 units above the first tile's max: exp2 against
+    the first-tile reference overflows, the workgroup recomputes exactly, and O_i = V[j*]."""
+    L, H = 600, 2
+    inp = gen.generate([L], H, seed=21, name="overflow")
+    i, jstar = 205, 555  # query in wave 6 of the first workgroup; key in tile 17
+    for h in range(H):
+        inp.k[jstar, h] = _bits(32.0 * bf16_bits_to_f64(inp.q[i, h]))
+    say("case overflow -> exact path")
+    out, lse = run_kernel(inp, gpu)
+    assert np.array_equal(out[i], inp.v[jstar])
+    compare(inp, out, lse, label="overflow")
+
+
+def test_very_negative_first_tile(gpu):
+    """The first key tile scores far below the rest for every query: later p would overflow
+    the first-tile reference."""
+    L, H = 300, 2
+    inp = gen.generate([L], H, seed=22, name="negfirst")
+    qmean = bf16_bits_to_f64(inp.q).mean(axis=0)  # [H, D]
+    for j in range(32):
+        for h in range(H):
+            inp.k[j, h] = _bits(-40.0 * qmean[h] / (np.abs(qmean[h]).max() + 1e-9))
+    say("case very negative first tile")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, label="negfirst")
+
+
+def test_large_but_finite_growth_stays_on_fast_path(gpu):
+    """Later keys score up to ~40 log2 units above the first tile (p up to ~2^40, no
+    overflow): the fixed-reference path must still match the oracle."""
+    L, H = 500, 2
+    inp = gen.generate([L], H, seed=23, name="growth")
+    rows = np.arange(100, 500, 7)
+    f = (inp.k[rows].astype(np.uint32) << 16).view(np.float32) * np.float32(4.0)
+    inp.k[rows] = _bits(f)
+    say("case large finite growth")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, label="growth")
