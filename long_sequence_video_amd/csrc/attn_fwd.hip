@@ -21,6 +21,9 @@
 //    ds_read_b64_tr_b16 in that same key order. No shuffles of P.
 //  * K and V tiles of 32 keys stream from global memory straight into an 8-slot LDS ring
 //    with 16-byte global_load_lds_dwordx4, four tiles ahead of use; one barrier per tile.
+//    A tile's row offset is uniform (scalar base), so the copies cost no vector ALU; the
+//    last, partial tile of a segment is loaded shifted to end at the segment end, and its
+//    leading keys (already counted in the previous tile) are masked.
 //  * Softmax in the exp2 domain: c = scale * log2(e) is folded into one fp32 FMA per score,
 //    p = exp2(s c - m c). The fast path fixes each row's reference m to the max of its
 //    first key tile and never moves it: later p may exceed 1, which floating point absorbs
@@ -118,6 +121,7 @@ struct Ctx {
   unsigned koff, voff;  // the byte offset inside that row
   int seg_len;
   float c;              // scale * log2(e)
+  unsigned kconst, vconst;  // krow * row_stride + koff, vrow * row_stride + voff
 };
 
 // Per-lane softmax state (query row l32, this lane's 16 of every 32 keys).
@@ -145,12 +149,25 @@ __device__ __forceinline__ void dma16(unsigned voff, const char* base, unsigned 
 // Workgroup barrier that waits for this wave's LDS reads but not for its prefetches.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Copy tile t (32 key rows of one head, rows past the segment repeat its last row) of K
-// and V into the ring slot at byte offset `slot`. Wave w copies rows 4w .. 4w+3 of each
-// (1 KB apiece); lane i writes 16-byte slot i of that block:
+// Tile copies. Wave w copies rows 4w .. 4w+3 of the 32-row tile of K and of V (1 KB
+// apiece) into the ring slot at byte offset `slot`; lane i writes 16-byte slot i of that
+// block:
 //   K block: slot i holds row 4w + i / 16, chunk (i % 16) ^ swz(row)   (XOR swizzle)
 //   V block: slot i holds row 4w + (i / 4) % 4, chunk 4 (i / 16) + i % 4 (column-block
 //            order: the 16 chunks of one 32-dim block of the 4 rows are contiguous)
+//
+// Segments of 32 keys or more: tile t holds rows min(32 t, seg_len - 32) .. +31, all inside
+// the segment (the last tile is shifted back to end at the segment end; tiles past the end,
+// which are prefetched but never used, repeat it). The row offset is uniform and goes into
+// the scalar base address; the lane's offset is a constant.
+__device__ __forceinline__ void load_tile_shifted(const Ctx& cx, int t, unsigned slot) {
+  const int start = min(t * kBK, cx.seg_len - kBK);
+  const unsigned off = (unsigned)start * cx.row_stride;
+  dma16(cx.kconst, cx.kbase + off, cx.lds_copy + slot);
+  dma16(cx.vconst, cx.vbase + off, cx.lds_copy + slot + kRingBytes);
+}
+
+// Segments shorter than 32 keys (a single tile): rows past the segment repeat its last row.
 __device__ __forceinline__ void load_tile_to(const Ctx& cx, int t, unsigned slot) {
   const int tkey = t * kBK, last = cx.seg_len - 1;
   const int kkey = tkey + cx.krow < last ? tkey + cx.krow : last;
@@ -159,9 +176,9 @@ __device__ __forceinline__ void load_tile_to(const Ctx& cx, int t, unsigned slot
   dma16(__umul24((unsigned)vkey, cx.row_stride) + cx.voff, cx.vbase, cx.lds_copy + slot + kRingBytes);
 }
 
-// Tile t into its ring slot t % kSlots.
+// Tile t into its ring slot t % kSlots (segments of 32 keys or more).
 __device__ __forceinline__ void load_tile(const Ctx& cx, int t) {
-  load_tile_to(cx, t, (unsigned)(t & (kSlots - 1)) * kSlotBytes);
+  load_tile_shifted(cx, t, (unsigned)(t & (kSlots - 1)) * kSlotBytes);
 }
 
 __device__ __forceinline__ bf16x8 lds_k(unsigned addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
@@ -206,6 +223,14 @@ __device__ __forceinline__ void mask_tail(f32x16& S, int valid, const Lane& ln) 
 #pragma unroll
   for (int v = 0; v < 16; ++v)
     if (8 * (v >> 2) + (v & 3) >= lim) S[v] = -INFINITY;
+}
+
+// The shifted last tile: its first `skip` keys were already counted in the tile before.
+__device__ __forceinline__ void mask_head(f32x16& S, int skip, const Lane& ln) {
+  const int lim = skip - 4 * ln.h32;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if (8 * (v >> 2) + (v & 3) < lim) S[v] = -INFINITY;
 }
 
 // This lane's max over its 16 scores of the tile.
@@ -288,8 +313,13 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
 // Returns false when this lane's sums or O are not finite (a p overflowed).
 __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, const bf16x8 (&qr)[8],
                                          const Lane& ln) {
+  if (n_kt >= 2) {
 #pragma unroll
-  for (int t = 0; t < kAhead; ++t) load_tile(cx, t);
+    for (int t = 0; t < kAhead; ++t) load_tile(cx, t);
+  } else {  // one tile of fewer than 32 keys (32 exactly is the same either way)
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) load_tile_to(cx, t, (unsigned)t * kSlotBytes);
+  }
   wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
   barrier_lds();
 #pragma unroll
@@ -334,20 +364,20 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
   if (t + 5 <= last) fast_step<6>(cx, t + 5, acc, SA, SB, PB, PA, nmc, qr, ln);
   if (t + 6 <= last) fast_step<7>(cx, t + 6, acc, SB, SA, PA, PB, nmc, qr, ln);
 
-  // Last tile (n_kt >= 2): P V of tile n_kt-2, masked exp2 of tile n_kt-1, its P V.
+  // Last tile (n_kt >= 2): P V of tile n_kt-2, masked exp2 of the shifted tile n_kt-1, its P V.
   const int tl = n_kt - 1;
   if (tl >= 1) {
     const unsigned vprev = ((tl - 1) & (kSlots - 1)) * kSlotBytes;
     const unsigned vlast = (tl & (kSlots - 1)) * kSlotBytes;
-    const int valid = cx.seg_len - tl * kBK;
+    const int skip = kBK - (cx.seg_len - tl * kBK);
     if (tl & 1) {
       pv_tile(acc.O, vprev, PA, ln);
-      mask_tail(SB, valid, ln);
+      mask_head(SB, skip, ln);
       softmax_all(SB, PB, acc.l, acc.lb, cx.c, nmc);
       pv_tile(acc.O, vlast, PB, ln);
     } else {
       pv_tile(acc.O, vprev, PB, ln);
-      mask_tail(SA, valid, ln);
+      mask_head(SA, skip, ln);
       softmax_all(SA, PA, acc.l, acc.lb, cx.c, nmc);
       pv_tile(acc.O, vlast, PA, ln);
     }
@@ -378,11 +408,15 @@ __device__ __forceinline__ void run_exact(const Ctx& cx, int n_kt, Acc& acc, con
   const float lazy = kLazyLog2 / cx.c;
   for (int t = 0; t < n_kt; ++t) {
     barrier_lds();  // every wave is done with slot 0
-    load_tile_to(cx, t, 0);
+    if (n_kt >= 2) load_tile_shifted(cx, t, 0);
+    else load_tile_to(cx, t, 0);
     wait_vmcnt<0>();
     barrier_lds();
     f32x16 S = qk_tile(0, qr, ln);
-    if (t == n_kt - 1) mask_tail(S, cx.seg_len - t * kBK, ln);
+    if (t == n_kt - 1) {
+      if (n_kt >= 2) mask_head(S, kBK - (cx.seg_len - t * kBK), ln);
+      else mask_tail(S, cx.seg_len, ln);
+    }
     const float mx = pair_max(lane_max(S));
     if (__builtin_amdgcn_ballot_w64(mx > acc.m + lazy) != 0) {  // wave-uniform
       const float mnew = fmaxf(acc.m, mx);
@@ -440,6 +474,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     cx.koff = (unsigned)(((i & 15) ^ swz(cx.krow)) * 16);
     cx.vrow = 4 * wave + ((i >> 2) & 3);
     cx.voff = (unsigned)((4 * (i >> 4) + (i & 3)) * 16);
+    cx.kconst = (unsigned)cx.krow * cx.row_stride + cx.koff;
+    cx.vconst = (unsigned)cx.vrow * cx.row_stride + cx.voff;
   }
   cx.seg_len = seg_len;
   cx.c = c;

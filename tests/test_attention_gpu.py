@@ -43,6 +43,7 @@ def test_tiny_config_all_rows(gpu):
     ([1, 0, 5, 0, 300, 2, 64], 3),
     ([1000], 4),
     ([200, 1700, 37], 2),
+    ([33, 40, 63, 65, 95, 97, 600], 2),
 ])
 def test_ragged_varlen_all_rows(gpu, seqlens, heads):
     inp = gen.generate(seqlens, heads, seed=77 + len(seqlens) + heads, name="ragged")
@@ -117,6 +118,21 @@ def test_dominant_logit_gives_exact_value_row(gpu):
     out, lse = run_kernel(inp, gpu)
     assert np.array_equal(out[i], inp.v[jstar]), (out[i][:, :8], inp.v[jstar][:, :8])
     compare(inp, out, lse, label="dominant")
+
+
+def test_dominant_key_in_last_tile_overlap_counted_once(gpu):
+    """The last, partial key tile is read shifted back to end at the segment end; its leading
+    rows belong to the tile before and must be counted once. A dominant key there gives
+    O_i = V[j*] and LSE_i = its scaled logit (+ ln 1): a double count would add ln 2."""
+    L, H = 600, 2  # tiles of 32: the last holds keys 576..599; rows 568..575 are re-read
+    inp = gen.generate([L], H, seed=31, name="overlap")
+    i, jstar = 40, 571
+    for h in range(H):
+        inp.k[jstar, h] = _bits(8.0 * bf16_bits_to_f64(inp.q[i, h]))
+    say("case dominant key in the re-read rows of the last tile")
+    out, lse = run_kernel(inp, gpu)
+    assert np.array_equal(out[i], inp.v[jstar])
+    compare(inp, out, lse, label="overlap")
 
 
 def test_identical_keys_mean_of_values(gpu):
