@@ -10,6 +10,11 @@ Workloads stand in for the MiniMax-H3 packed clips the pages describe
 blocks with 56 heads x 128; the 544x960x124 clip packs to 19,394 tokens;
 FastVideo perf/ulysses-h3-adaptive commit message: sp=4 gives one rank 14 of
 the 56 heads). Tensor ids: Q = 0, K = 1, V = 2, boosted-K row choice = 3.
+
+The QKV-prologue inputs (FastVideo #2049, MotionKernel ``qkv_prologue`` and its
+tests) add per-head norm weights (ids 4, 5) and cos/sin tables: either the usual
+rotate-half RoPE angles, or iid N(0,1) tables (ids 6, 7) as the page's own
+kernel test draws them.
 """
 
 from __future__ import annotations
@@ -26,6 +31,7 @@ LIB_PATH = os.path.join(_HERE, "liblsvgen.so")
 SOURCE_PATH = os.path.join(_HERE, "gen.c")
 
 Q_ID, K_ID, V_ID, CHOOSE_ID = 0, 1, 2, 3
+QW_ID, KW_ID, COS_ID, SIN_ID = 4, 5, 6, 7
 RMS_EPS = 1e-5  # the H3 QK-norm eps (FastVideo #2049, MotionKernel qkv prologue)
 
 _lib = None
@@ -212,3 +218,92 @@ def make_config(name: str) -> Inputs:
     if name not in CONFIGS:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(CONFIGS)}")
     return generate(name=name, **CONFIGS[name])
+
+
+# ---------------------------------------------------------------- QKV prologue inputs
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """fp64 -> fp32 (round to nearest even) -> bf16 bits (round to nearest even)."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def rope_tables(seq_len: int, rotary_dim: int, *, base: float = 10000.0, start: int = 0):
+    """cos/sin tables ``[S, R]`` (bf16 bits) in the rotate-half layout: channels i and
+    i + R/2 share the angle ``(start + s) * base^(-2 i / R)``."""
+    if rotary_dim % 2:
+        raise ValueError("rotary_dim must be even")
+    h = rotary_dim // 2
+    inv_freq = base ** (-2.0 * np.arange(h, dtype=np.float64) / max(rotary_dim, 1))
+    ang = (start + np.arange(seq_len, dtype=np.float64))[:, None] * inv_freq[None, :]
+    ang = np.concatenate([ang, ang], axis=1)
+    return f64_to_bf16_bits(np.cos(ang)), f64_to_bf16_bits(np.sin(ang))
+
+
+@dataclass
+class PrologueInputs:
+    """One QKV-prologue workload (bf16 bit patterns)."""
+    name: str
+    q: np.ndarray          # uint16 [B, S, H, D]
+    k: np.ndarray
+    v: np.ndarray
+    q_weight: np.ndarray   # uint16 [D]
+    k_weight: np.ndarray
+    cos: np.ndarray        # uint16 [S, R]
+    sin: np.ndarray
+    eps: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        return tuple(int(x) for x in self.q.shape)
+
+    @property
+    def rotary_dim(self) -> int:
+        return int(self.cos.shape[1])
+
+    def algorithmic_bytes(self) -> int:
+        """HBM bytes of one pass: q, k, v read and the three planes written once (bf16),
+        plus the cos/sin rows and the two weights."""
+        b, s, h, d = self.shape
+        return 6 * b * s * h * d * 2 + 2 * s * self.rotary_dim * 2 + 2 * d * 2
+
+
+def generate_prologue(batch: int, seq_len: int, heads: int, head_dim: int = 128, rotary_dim: int = 96, *,
+                      seed: int, tables: str = "rope", eps: float = RMS_EPS, name: str = "prologue") -> PrologueInputs:
+    """q, k, v iid N(0,1) ``[B, S, H, D]`` (streams (seed, 0/1/2)); norm weights iid N(0,1)
+    (streams 4, 5; the page's test draws them so, which also covers negative weights);
+    ``tables="rope"``: RoPE angles from position 0, ``"normal"``: iid N(0,1) tables
+    (streams 6, 7)."""
+    shape = (batch, seq_len, heads, head_dim)
+    n = batch * seq_len * heads * head_dim
+    q = normal_bf16(n, seed, Q_ID).reshape(shape)
+    k = normal_bf16(n, seed, K_ID).reshape(shape)
+    v = normal_bf16(n, seed, V_ID).reshape(shape)
+    qw = normal_bf16(head_dim, seed, QW_ID)
+    kw = normal_bf16(head_dim, seed, KW_ID)
+    if tables == "rope":
+        cos, sin = rope_tables(seq_len, rotary_dim)
+    elif tables == "normal":
+        cos = normal_bf16(seq_len * rotary_dim, seed, COS_ID).reshape(seq_len, rotary_dim)
+        sin = normal_bf16(seq_len * rotary_dim, seed, SIN_ID).reshape(seq_len, rotary_dim)
+    else:
+        raise ValueError("tables must be 'rope' or 'normal'")
+    return PrologueInputs(name, q, k, v, qw, kw, cos, sin, float(eps), {"seed": seed, "tables": tables})
+
+
+# QKV-prologue workloads: the page's kernel-test shape (512 tokens, random tables), the
+# varlen pack's 161,394 tokens as one [1, S] sequence with RoPE tables (the bench
+# workload), and the page's int32-plane test shape (4 x 40,000 x 56 x 128).
+PROLOGUE_CONFIGS = {
+    "prologue_s512_h56_randtab": dict(batch=1, seq_len=512, heads=56, seed=2001, tables="normal"),
+    "prologue_s161394_h56": dict(batch=1, seq_len=161394, heads=56, seed=2002),
+    "prologue_b4_s40000_h56": dict(batch=4, seq_len=40000, heads=56, seed=2003, tables="normal"),
+}
+
+
+def make_prologue_config(name: str) -> PrologueInputs:
+    if name not in PROLOGUE_CONFIGS:
+        raise KeyError(f"unknown prologue workload {name!r}; known: {sorted(PROLOGUE_CONFIGS)}")
+    return generate_prologue(name=name, **PROLOGUE_CONFIGS[name])
