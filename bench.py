@@ -6,7 +6,13 @@ clips, 19,394 + 38,000 + 104,000 tokens x 56 heads x 128 (161,394 tokens; 3.623e
 per step). Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                  [--no-prologue] [--prologue-only]
   python bench.py --copy-bytes N   # a plain device copy of N bytes, to calibrate HBM counters
+
+A second object, ``qkv_prologue``, times the fused QKV prologue (QK RMSNorm + partial RoPE +
+V copy, the pass that feeds attention) on the same token count: 161,394 tokens x 56 heads x
+128, rotary width 96. It is bound by HBM and reported in GB/s against 8 TB/s; it is not
+part of ``value``.
 
 roofline.traffic (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
 summary committed under profiles/ for this workload, scaled by the same counters on a copy of
@@ -35,17 +41,18 @@ EXTRA_CONFIGS = {"h56_s104000": dict(seqlens=[104000], heads=56, seed=1005)}
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "long_sequence_video_amd", "csrc", "attn_fwd.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_{workload}_hbm_traffic.md")
+PROLOGUE_SOURCE = os.path.join(ROOT, "long_sequence_video_amd", "csrc", "qkv_prologue.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "{kernel}_{workload}_hbm_traffic.md")
 
 
-def kernel_source_sha256() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel_source: str = KERNEL_SOURCE, kernel: str = "attn_fwd"):
     """(bytes per launch, summary path) from the committed counter summary, if it was taken
     on the current kernel source; else (None, reason)."""
-    path = TRAFFIC_SUMMARY.format(workload=workload)
+    path = TRAFFIC_SUMMARY.format(kernel=kernel, workload=workload)
     if not os.path.exists(path):
         return None, "no counter summary for this workload"
     fields = {}
@@ -53,7 +60,7 @@ def measured_traffic(workload: str):
         if line.startswith("- ") and ":" in line:
             key, val = line[2:].split(":", 1)
             fields[key.strip()] = val.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+    if fields.get("kernel_source_sha256") != kernel_source_sha256(kernel_source):
         return None, "counter summary predates the current kernel source"
     try:
         return float(fields["hbm_bytes_per_launch"]), os.path.relpath(path, ROOT)
@@ -72,6 +79,55 @@ def copy_calibration(nbytes: int, steps: int):
         dst.copy_(src)
     torch.cuda.synchronize(dev)
     print(json.dumps({"copy_bytes": nbytes, "launches": steps}), flush=True)
+
+
+PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth (8 TB/s)
+PROLOGUE_CONFIG = "prologue_s161394_h56"
+
+
+def bench_prologue(steps: int, warmup: int):
+    """Time the fused QKV prologue on its bench workload; returns the JSON object."""
+    import torch
+    import long_sequence_video_amd as lsv
+    from long_sequence_video_amd import inputs as gen
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    inp = gen.make_prologue_config(PROLOGUE_CONFIG)
+    log(f"generated {PROLOGUE_CONFIG} in {time.perf_counter() - t0:.1f} s")
+    to = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    q, k, v, qw, kw, cos, sin = (to(x) for x in (inp.q, inp.k, inp.v, inp.q_weight, inp.k_weight, inp.cos, inp.sin))
+    b, s, h, d = inp.shape
+    out = torch.empty((3 * b, s, h, d), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        lsv.qkv_prologue(q, k, v, qw, kw, cos, sin, eps=inp.eps, out=out)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = inp.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"{PROLOGUE_CONFIG}: {ms:.3f} ms, {gbs:.0f} GB/s, {100 * gbs / PEAK_HBM_GBS:.1f}% of HBM peak")
+    traffic, traffic_src = measured_traffic(PROLOGUE_CONFIG, kernel_source=PROLOGUE_SOURCE, kernel="qkv_prologue")
+    del q, k, v, qw, kw, cos, sin, out
+    torch.cuda.empty_cache()
+    return {
+        "workload": PROLOGUE_CONFIG, "shape": [b, s, h, d], "rotary_dim": inp.rotary_dim,
+        "ms_per_call": round(ms, 4), "steps": steps,
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_unit": "HBM bytes per launch",
+            "traffic_source": traffic_src, "algorithmic_hbm_bytes": nbytes, "kernel": "qkv_prologue_kernel",
+        },
+    }
 
 
 def log(*a):
@@ -142,6 +198,8 @@ def main():
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0, help="run the counter-calibration copy instead")
+    ap.add_argument("--no-prologue", action="store_true", help="skip the QKV-prologue leg")
+    ap.add_argument("--prologue-only", action="store_true", help="time only the QKV prologue (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward of one rank's share runs on a "
@@ -160,6 +218,9 @@ def main():
         from long_sequence_video_amd.build import build
         build()
     dev = torch.device("cuda:0")
+    if args.prologue_only:
+        print(json.dumps({"qkv_prologue": bench_prologue(args.steps, args.warmup)}), flush=True)
+        return
 
     t0 = time.perf_counter()
     inp = make_inputs(args.config)
@@ -236,6 +297,8 @@ def main():
     }
     del q, k, v, out, lse
     torch.cuda.empty_cache()
+    if not args.no_prologue:
+        result["qkv_prologue"] = bench_prologue(max(args.steps, 10), max(args.warmup, 2))
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(inp)

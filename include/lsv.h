@@ -1,4 +1,5 @@
-/* lsv: dense non-causal varlen BF16 attention forward for AMD MI355X (gfx950).
+/* lsv: dense non-causal varlen BF16 attention forward for AMD MI355X (gfx950), and the
+ * fused QKV prologue (QK RMSNorm + partial RoPE) that feeds it.
  *
  * The operation (FastVideo #2049, diff of fastvideo/attention/utils/flash_attn_cute.py,
  * the varlen forward wrapper; TensorRT-LLM PR #21275, Description): for every packed
@@ -63,6 +64,39 @@ enum lsv_status {
 int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
                  float scale, void* stream);
+
+/* Fused QKV prologue on the caller's stream (asynchronous).
+ *
+ * The operation (FastVideo #2049, diff of
+ * fastvideo/models/dits/minimax_h3_fusions/mk/qkv_prologue.py, module docstring and kernel;
+ * MiniMaxH3Attention.forward on the same page rotates 96 of the 128 channels): every
+ * (batch, position s, head) row x of Q, and of K with its own weight, becomes
+ *     y_i   = x_i * rsqrt(mean_d x_d^2 + eps) * w_i
+ *     out_i = y_i cos[s,i] - y_{i+R/2} sin[s,i]     for i < R/2
+ *     out_i = y_i cos[s,i] + y_{i-R/2} sin[s,i]     for R/2 <= i < R
+ *     out_i = y_i                                    for i >= R
+ * computed in fp32 and rounded once to bf16 (nearest even); V is copied unchanged. The
+ * three results are stacked [3, batch, seq_len, n_heads, head_dim] (plane 0 Q, 1 K, 2 V),
+ * the layout the page's attention path consumes.
+ *
+ * q, k, v      device pointers, bf16 [batch, seq_len, n_heads, head_dim], 16-byte aligned.
+ * q_weight, k_weight  device pointers, bf16 [head_dim] (the per-head norm weights).
+ * cos, sin     device pointers, bf16 [seq_len, rotary_dim], 16-byte aligned; row s serves
+ *              position s of every batch row and head. May be NULL when rotary_dim is 0.
+ * out          device pointer, bf16 [3, batch, seq_len, n_heads, head_dim], 16-byte aligned,
+ *              not overlapping any input. Fully written.
+ * batch, seq_len  >= 0 (either 0: successful no-op); batch * seq_len * n_heads < 2^31.
+ * n_heads      >= 1.
+ * head_dim     must be 128.
+ * rotary_dim   R: a multiple of 16 in [0, 128] (96 for the H3 blocks), else UNSUPPORTED.
+ * eps          finite, >= 0 (1e-5 for the H3 blocks). With eps = 0 an all-zero row gives NaN.
+ * stream       a hipStream_t, or NULL for the default stream.
+ *
+ * Validation happens before any HIP call; on error nothing is launched.
+ */
+int lsv_qkv_prologue(const void* q, const void* k, const void* v, const void* q_weight, const void* k_weight,
+                     const void* cos, const void* sin, void* out, int64_t batch, int64_t seq_len, int32_t n_heads,
+                     int32_t head_dim, int32_t rotary_dim, float eps, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* lsv_status_string(int status);

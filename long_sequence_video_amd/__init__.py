@@ -1,11 +1,12 @@
-"""lsv: dense non-causal varlen BF16 attention forward for MI355X (gfx950).
+"""lsv: dense non-causal varlen BF16 attention forward for MI355X (gfx950), and the fused
+QKV prologue (QK RMSNorm + partial RoPE) that feeds it.
 
 Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in-tree by
 ``python -m long_sequence_video_amd.build``). The functions named like the C entry points
-(``lsv_attn_fwd``, ``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only
-marshal arguments; ``attn_fwd`` adds torch-tensor conveniences (output allocation, the
-current stream). There is no fallback: if the library is missing or a call fails, an
-exception is raised.
+(``lsv_attn_fwd``, ``lsv_qkv_prologue``, ``lsv_status_string``, ``lsv_device_peak``,
+``lsv_tile_config``) only marshal arguments; ``attn_fwd`` and ``qkv_prologue`` add
+torch-tensor conveniences (output allocation, the current stream). There is no fallback:
+if the library is missing or a call fails, an exception is raised.
 """
 
 from __future__ import annotations
@@ -15,12 +16,13 @@ import math
 import os
 
 __all__ = [
-    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_status_string", "lsv_device_peak",
-    "lsv_tile_config", "attn_fwd", "flops", "EXPORTED_SYMBOLS",
+    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_qkv_prologue", "lsv_status_string",
+    "lsv_device_peak", "lsv_tile_config", "attn_fwd", "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
-EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_status_string", "lsv_device_peak", "lsv_tile_config")
+EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak",
+                    "lsv_tile_config")
 
 LSV_OK = 0
 LSV_ERR_INVALID_ARG = -1
@@ -51,6 +53,8 @@ def load_library(path: str = LIB_PATH):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.lsv_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, vp]
     lib.lsv_attn_fwd.restype = ctypes.c_int
+    lib.lsv_qkv_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_float, vp]
+    lib.lsv_qkv_prologue.restype = ctypes.c_int
     lib.lsv_status_string.argtypes = [ctypes.c_int]
     lib.lsv_status_string.restype = ctypes.c_char_p
     lib.lsv_device_peak.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
@@ -67,6 +71,14 @@ def lsv_attn_fwd(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, n_se
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().lsv_attn_fwd(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads,
                                        head_dim, scale, stream)
+
+
+def lsv_qkv_prologue(q: int, k: int, v: int, q_weight: int, k_weight: int, cos: int, sin: int, out: int,
+                     batch: int, seq_len: int, n_heads: int, head_dim: int, rotary_dim: int, eps: float,
+                     stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_qkv_prologue(q, k, v, q_weight, k_weight, cos, sin, out, batch, seq_len, n_heads,
+                                           head_dim, rotary_dim, eps, stream)
 
 
 def lsv_status_string(status: int) -> str:
@@ -144,3 +156,51 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | 
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_attn_fwd")
     return out, lse
+
+
+def qkv_prologue(q, k, v, q_weight, k_weight, cos, sin, *, eps: float = 1e-5, out=None, stream=None):
+    """Fused QK RMSNorm + partial rotate-half RoPE, and the V copy, on torch tensors.
+
+    Args:
+      q, k, v: bfloat16 ``[B, S, H, 128]`` (or ``[S, H, 128]``), contiguous, one GPU.
+      q_weight, k_weight: bfloat16 ``[128]``.
+      cos, sin: bfloat16 ``[S, R]`` (R a multiple of 16, at most 128), or ``None`` for R = 0.
+      eps: the RMSNorm epsilon (1e-5 for the H3 blocks).
+      out: optional preallocated ``[3 B, S, H, 128]`` (``[3, S, H, 128]`` for 3-D inputs).
+      stream: a ``torch.cuda.Stream``; default: the current stream.
+
+    Returns:
+      the stacked output: rotated Q, rotated K, V.
+    """
+    import torch
+    if q.dim() not in (3, 4) or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, S, H, D] (or [S, H, D]) shape")
+    tensors = [q, k, v, q_weight, k_weight] + ([cos, sin] if cos is not None else [])
+    if any(t.dtype != torch.bfloat16 for t in tensors):
+        raise ValueError("all inputs must be bfloat16")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all inputs must be contiguous")
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must be on the same GPU")
+    b, s, h, d = (1, *q.shape) if q.dim() == 3 else tuple(q.shape)
+    if (cos is None) != (sin is None):
+        raise ValueError("cos and sin must both be given or both be None")
+    rd = 0 if cos is None else int(cos.shape[-1])
+    if cos is not None and (cos.shape != sin.shape or cos.dim() != 2 or cos.shape[0] != s):
+        raise ValueError("cos/sin must be [S, R] tables")
+    if q_weight.shape != (d,) or k_weight.shape != (d,):
+        raise ValueError("norm weights must be [head_dim]")
+    shape = (3, s, h, d) if q.dim() == 3 else (3 * b, s, h, d)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    if tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != dev:
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {shape}")
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lsv_qkv_prologue(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_weight.data_ptr(), k_weight.data_ptr(),
+                              0 if cos is None else cos.data_ptr(), 0 if sin is None else sin.data_ptr(),
+                              out.data_ptr(), b, s, h, d, rd, eps, st.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_qkv_prologue")
+    return out

@@ -1,6 +1,7 @@
 """Build the native libraries in-tree.
 
-* ``liblsv.so``  — the HIP attention library (C ABI in ``include/lsv.h``), gfx950 only.
+* ``liblsv.so``  — the HIP library (attention forward, QKV prologue; C ABI in
+  ``include/lsv.h``), gfx950 only.
 * ``inputs/liblsvgen.so`` — the seeded input generator (plain C, OpenMP).
 
 Run ``python -m long_sequence_video_amd.build``. Every call recompiles.
@@ -15,7 +16,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-HIP_SOURCE = os.path.join(PKG, "csrc", "attn_fwd.hip")
+HIP_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("attn_fwd.hip", "qkv_prologue.hip")]
 HIP_LIB = os.path.join(PKG, "liblsv.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
@@ -43,7 +44,7 @@ def hip_flags() -> list[str]:
 
 def build_hip(verbose: bool = False) -> str:
     tmp = HIP_LIB + ".tmp"
-    cmd = [hipcc(), *hip_flags(), HIP_SOURCE, "-o", tmp]
+    cmd = [hipcc(), *hip_flags(), *HIP_SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

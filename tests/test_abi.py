@@ -63,6 +63,8 @@ A = 1 << 20
     (dict(o=A + 2), lsv.LSV_ERR_ALIGNMENT),
     (dict(lse=A + 2), lsv.LSV_ERR_ALIGNMENT),
     (dict(total_tokens=1 << 31), lsv.LSV_ERR_UNSUPPORTED),
+    # one head's K/V rows of a segment must be addressable with 32-bit byte offsets
+    (dict(max_seqlen=299_594, total_tokens=299_594, n_heads=56), lsv.LSV_ERR_UNSUPPORTED),
     # successful no-ops: nothing to compute, nothing launched
     (dict(n_seqs=0), lsv.LSV_OK),
     (dict(max_seqlen=0), lsv.LSV_OK),
@@ -81,3 +83,36 @@ def test_validation_before_any_hip_call(args, code):
 def test_flops_count():
     assert lsv.flops([19394, 38000, 104000], 56) == 4 * (19394 ** 2 + 38000 ** 2 + 104000 ** 2) * 56 * 128
     assert lsv.flops([104000], 56) == 4 * 104000 ** 2 * 56 * 128
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(rotary_dim=40), lsv.LSV_ERR_UNSUPPORTED),       # not a multiple of 16
+    (dict(rotary_dim=144), lsv.LSV_ERR_UNSUPPORTED),      # wider than the head
+    (dict(rotary_dim=-16), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(batch=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(seq_len=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(eps=-1e-5), lsv.LSV_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(q=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(k_weight=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(out=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(cos=0), lsv.LSV_ERR_INVALID_ARG),               # tables are needed when rotary_dim > 0
+    (dict(k=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(sin=A + 4), lsv.LSV_ERR_ALIGNMENT),
+    (dict(q_weight=A + 1), lsv.LSV_ERR_ALIGNMENT),
+    (dict(batch=4, seq_len=40000, n_heads=14000), lsv.LSV_ERR_UNSUPPORTED),  # 2^31 rows or more
+    (dict(batch=1 << 40, seq_len=1 << 40), lsv.LSV_ERR_UNSUPPORTED),          # no overflow in the check
+    # successful no-ops
+    (dict(batch=0), lsv.LSV_OK),
+    (dict(seq_len=0, q=0, k=0, v=0, out=0), lsv.LSV_OK),
+])
+def test_prologue_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, q_weight=A, k_weight=A, cos=A, sin=A, out=A, batch=1, seq_len=10, n_heads=4,
+             head_dim=128, rotary_dim=96, eps=1e-5)
+    a.update(args)
+    rc = lsv.lsv_qkv_prologue(a["q"], a["k"], a["v"], a["q_weight"], a["k_weight"], a["cos"], a["sin"], a["out"],
+                              a["batch"], a["seq_len"], a["n_heads"], a["head_dim"], a["rotary_dim"], a["eps"], None)
+    assert rc == code
