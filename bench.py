@@ -6,8 +6,14 @@ clips, 19,394 + 38,000 + 104,000 tokens x 56 heads x 128 (161,394 tokens; 3.623e
 per step). Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
-                  [--no-prologue] [--prologue-only]
+                  [--no-prologue] [--prologue-only] [--no-bwd] [--bwd-only]
   python bench.py --copy-bytes N   # a plain device copy of N bytes, to calibrate HBM counters
+
+An object ``attn_bwd`` times the backward (dQ, dK, dV; deterministic, three kernels) on the
+same pack, counted the usual way as 2.5 x the forward's flops (the five products of the
+textbook backward); the kernels execute seven products (the dQ pass recomputes S and dP
+instead of accumulating dQ with atomics), reported as ``mfma_flops_executed``. O and LSE
+come from the forward kernel. Not part of ``value``.
 
 A second object, ``qkv_prologue``, times the fused QKV prologue (QK RMSNorm + partial RoPE +
 V copy, the pass that feeds attention) on the same token count: 161,394 tokens x 56 heads x
@@ -130,6 +136,54 @@ def bench_prologue(steps: int, warmup: int):
     }
 
 
+def bench_backward(name: str, steps: int, warmup: int):
+    """Time the attention backward on workload ``name``; returns the JSON object."""
+    import torch
+    import long_sequence_video_amd as lsv
+    from long_sequence_video_amd import inputs as gen
+    dev = torch.device("cuda:0")
+    inp = make_inputs(name)
+    do_bits = gen.normal_bf16(inp.q.size, 7, 9).reshape(inp.q.shape)
+    to = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    q, k, v, do = to(inp.q), to(inp.k), to(inp.v), to(do_bits)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    out, lse = lsv.attn_fwd(q, k, v, cu, inp.max_seqlen, inp.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(lsv.lsv_attn_bwd_workspace_size(inp.total_tokens, inp.n_heads), dtype=torch.uint8, device=dev)
+
+    def step():
+        lsv.attn_bwd(q, k, v, out, do, lse, cu, inp.max_seqlen, inp.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    fwd = inp.flops()
+    counted = 2.5 * fwd
+    executed = 3.5 * fwd
+    tf = counted / (ms * 1e-3) / 1e12
+    tf_exec = executed / (ms * 1e-3) / 1e12
+    log(f"{name} backward: {ms:.3f} ms, {tf:.1f} TFLOP/s counted (2.5 x fwd), {tf_exec:.1f} executed, "
+        f"{100 * tf_exec / PEAK_BF16_TFLOPS:.1f}% of peak")
+    del q, k, v, do, out, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": name, "ms_per_step": round(ms, 4), "steps": steps,
+        "tflops_counted": round(tf, 2), "flops_counted": counted, "counting": "2.5 x sum 4*S^2*H*D",
+        "mfma_flops_executed": executed,
+        "roofline": {"bound": "mfma", "achieved": round(tf_exec, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+                     "kernels": ["bwd_prep_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"]},
+    }
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -200,6 +254,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0, help="run the counter-calibration copy instead")
     ap.add_argument("--no-prologue", action="store_true", help="skip the QKV-prologue leg")
     ap.add_argument("--prologue-only", action="store_true", help="time only the QKV prologue (for profiling)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
+    ap.add_argument("--bwd-only", action="store_true", help="time only the backward (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward of one rank's share runs on a "
@@ -220,6 +276,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.prologue_only:
         print(json.dumps({"qkv_prologue": bench_prologue(args.steps, args.warmup)}), flush=True)
+        return
+    if args.bwd_only:
+        print(json.dumps({"attn_bwd": bench_backward(args.config, args.steps, args.warmup)}), flush=True)
         return
 
     t0 = time.perf_counter()
@@ -297,6 +356,8 @@ def main():
     }
     del q, k, v, out, lse
     torch.cuda.empty_cache()
+    if not args.no_bwd:
+        result["attn_bwd"] = bench_backward(args.config, min(max(args.steps, 3), 5), max(min(args.warmup, 2), 1))
     if not args.no_prologue:
         result["qkv_prologue"] = bench_prologue(max(args.steps, 10), max(args.warmup, 2))
     if not args.no_cpu_baseline:

@@ -1,5 +1,5 @@
-/* lsv: dense non-causal varlen BF16 attention forward for AMD MI355X (gfx950), and the
- * fused QKV prologue (QK RMSNorm + partial RoPE) that feeds it.
+/* lsv: dense non-causal varlen BF16 attention forward and backward for AMD MI355X (gfx950),
+ * and the fused QKV prologue (QK RMSNorm + partial RoPE) that feeds them.
  *
  * The operation (FastVideo #2049, diff of fastvideo/attention/utils/flash_attn_cute.py,
  * the varlen forward wrapper; TensorRT-LLM PR #21275, Description): for every packed
@@ -64,6 +64,44 @@ enum lsv_status {
 int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
                  float scale, void* stream);
+
+/* Workspace bytes lsv_attn_bwd needs: two fp32 values per (head, token), i.e.
+ * 8 * total_tokens * n_heads. Returns -1 for a negative size or n_heads < 1. */
+int64_t lsv_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads);
+
+/* Attention backward on the caller's stream (asynchronous; three kernels, no atomics: the
+ * same inputs give bit-identical gradients on every run).
+ *
+ * The operation (FastVideo #2049, diff of fastvideo/attention/utils/flash_attn_cute.py, the
+ * varlen backward op: it takes q, k, v, out, dout, lse, the softmax scale, causal=False and
+ * the forward's cu_seqlens / max_seqlen, and returns dq, dk, dv shaped like q, k, v; the
+ * page's test fakes pin that argument list). For every segment, head, query i and key j of
+ * the segment, with P_ij = exp(scale q_i.k_j - LSE_i):
+ *     D_i   = dO_i . O_i
+ *     dS_ij = P_ij (dO_i . v_j - D_i)
+ *     dQ_i  = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i
+ * P is computed in fp32 from the given fp32 LSE; P (for dV) and dS (for dQ, dK) are rounded
+ * to bf16 for the matrix products, which accumulate in fp32; the gradients are rounded to
+ * bf16 (nearest even).
+ *
+ * q, k, v, o, dout  device pointers, bf16 [total_tokens, n_heads, head_dim], 16-byte aligned;
+ *              o and lse are the forward's outputs for these q, k, v (lsv_attn_fwd).
+ * lse          device pointer, fp32 [n_heads, total_tokens].
+ * dq, dk, dv   device pointers, bf16, same layout as q, 16-byte aligned. Written for every
+ *              token row inside a segment; other rows untouched.
+ * cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale: as for
+ *              lsv_attn_fwd (same limits and the same skipped-segment rule).
+ * workspace    device pointer, 4-byte aligned, at least lsv_attn_bwd_workspace_size bytes
+ *              (else LSV_ERR_INVALID_ARG); overwritten. Owned by the caller.
+ * stream       a hipStream_t, or NULL for the default stream.
+ *
+ * total_tokens * n_heads must stay below 2^31 (else LSV_ERR_UNSUPPORTED). Validation happens
+ * before any HIP call; on error nothing is launched.
+ */
+int lsv_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                 int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale, void* workspace,
+                 int64_t workspace_bytes, void* stream);
 
 /* Fused QKV prologue on the caller's stream (asynchronous).
  *

@@ -16,13 +16,14 @@ import math
 import os
 
 __all__ = [
-    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_qkv_prologue", "lsv_status_string",
-    "lsv_device_peak", "lsv_tile_config", "attn_fwd", "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
+    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size",
+    "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak", "lsv_tile_config", "attn_fwd", "attn_bwd",
+    "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
-EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak",
-                    "lsv_tile_config")
+EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue",
+                    "lsv_status_string", "lsv_device_peak", "lsv_tile_config")
 
 LSV_OK = 0
 LSV_ERR_INVALID_ARG = -1
@@ -53,6 +54,10 @@ def load_library(path: str = LIB_PATH):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.lsv_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, vp]
     lib.lsv_attn_fwd.restype = ctypes.c_int
+    lib.lsv_attn_bwd.argtypes = [vp] * 10 + [i32, i32, i64, i32, i32, ctypes.c_float, vp, i64, vp]
+    lib.lsv_attn_bwd.restype = ctypes.c_int
+    lib.lsv_attn_bwd_workspace_size.argtypes = [i64, i32]
+    lib.lsv_attn_bwd_workspace_size.restype = i64
     lib.lsv_qkv_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_float, vp]
     lib.lsv_qkv_prologue.restype = ctypes.c_int
     lib.lsv_status_string.argtypes = [ctypes.c_int]
@@ -71,6 +76,18 @@ def lsv_attn_fwd(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, n_se
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().lsv_attn_fwd(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads,
                                        head_dim, scale, stream)
+
+
+def lsv_attn_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, cu_seqlens: int,
+                 n_seqs: int, max_seqlen: int, total_tokens: int, n_heads: int, head_dim: int, scale: float,
+                 workspace: int, workspace_bytes: int, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, n_seqs, max_seqlen,
+                                       total_tokens, n_heads, head_dim, scale, workspace, workspace_bytes, stream)
+
+
+def lsv_attn_bwd_workspace_size(total_tokens: int, n_heads: int) -> int:
+    return load_library().lsv_attn_bwd_workspace_size(total_tokens, n_heads)
 
 
 def lsv_qkv_prologue(q: int, k: int, v: int, q_weight: int, k_weight: int, cos: int, sin: int, out: int,
@@ -204,3 +221,64 @@ def qkv_prologue(q, k, v, q_weight, k_weight, cos, sin, *, eps: float = 1e-5, ou
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_qkv_prologue")
     return out
+
+
+def attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None = None, scale: float | None = None, *,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward on torch tensors (all on one GPU).
+
+    Args:
+      q, k, v, out, dout: bfloat16 ``[total_tokens, n_heads, 128]``, contiguous (``out`` and
+        ``lse`` from ``attn_fwd`` on the same q, k, v).
+      lse: float32 ``[n_heads, total_tokens]``.
+      cu_seqlens, max_seqlen, scale: as for ``attn_fwd``.
+      dq, dk, dv: optional preallocated gradients (shaped like q).
+      workspace: optional uint8 device buffer of at least ``lsv_attn_bwd_workspace_size`` bytes.
+      stream: a ``torch.cuda.Stream``; default: the current stream.
+
+    Returns:
+      ``(dq, dk, dv)``.
+    """
+    import torch
+    tensors = (q, k, v, out, dout)
+    if any(t.dtype != torch.bfloat16 for t in tensors):
+        raise ValueError("q, k, v, out, dout must be bfloat16")
+    if q.dim() != 3 or any(t.shape != q.shape for t in tensors):
+        raise ValueError("q, k, v, out, dout must share one [total_tokens, heads, head_dim] shape")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("q, k, v, out, dout must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in (*tensors, lse, cu_seqlens)):
+        raise ValueError("all tensors must be on the same GPU")
+    total, heads, dim = q.shape
+    if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for g in (dq, dk, dv):
+        if g.shape != q.shape or g.dtype != torch.bfloat16 or not g.is_contiguous() or g.device != dev:
+            raise ValueError("dq, dk, dv must be contiguous bfloat16 tensors shaped like q")
+    need = lsv_attn_bwd_workspace_size(total, heads)
+    if need < 0:
+        raise ValueError("invalid sizes")
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device buffer")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                          max_seqlen, total, heads, dim, scale, workspace.data_ptr(), ws_bytes, s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_bwd")
+    return dq, dk, dv

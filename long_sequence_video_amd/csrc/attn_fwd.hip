@@ -45,8 +45,11 @@
 #include <math.h>
 
 #include "lsv.h"
+#include "tile_ops.h"
 
 namespace {
+
+using namespace lsv_tiles;
 
 constexpr int kD = 128;                       // head dim
 constexpr int kWaveQ = 32;                    // query rows per wave
@@ -56,8 +59,7 @@ constexpr int kBK = 32;                       // keys per tile
 constexpr int kSlots = 8;                     // LDS ring slots (K and V each)
 constexpr int kAhead = 4;                     // tiles in flight ahead of use
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowBytes = kD * 2;             // 256
-constexpr int kSlotBytes = kBK * kRowBytes;   // 8 KB
+constexpr int kSlotBytes = kTileBytes;        // 8 KB: 32 key rows of 256 bytes
 constexpr int kRingBytes = kSlots * kSlotBytes;
 constexpr int kLdsBytes = 2 * kRingBytes + 64;  // K ring, V ring (128 KB), workgroup flags
 constexpr int kCopies = kSlotBytes / 1024 / kWaves;  // 1 KB copies per wave per tile, for K and for V
@@ -65,45 +67,6 @@ constexpr int kOpsPerTile = 2 * kCopies;             // memory instructions per 
 constexpr float kLazyLog2 = 8.0f;             // exact path: raise the running max only beyond this
 static_assert(kCopies == 1, "one 1 KB copy per wave per tile");
 static_assert(kAhead >= 2 && kAhead <= kSlots - 2, "ring too small for the prefetch distance");
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) int lds_int;
-
-// 16-byte chunk swizzle of a K row in LDS: chunk c of row r lives at chunk c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Nothing may be scheduled across this point (keeps the hand-placed MFMA / VALU interleave).
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-// max / sum with the partner lane l ^ 32 (same query, the other 16 keys of each 32).
-__device__ __forceinline__ float pair_max(float x) {
-  u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Wait until at most N of this wave's memory loads are outstanding (they complete in order).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 struct Lane {
   int lane, h32, l32;
@@ -131,23 +94,6 @@ struct Acc {
   float l;      // sum of fp32 p: for the LSE
   float lb;     // sum of bf16(p), the weights P V used: normalises O
 };
-
-// 16-byte global -> LDS copy per lane from base + voff: lane i writes LDS bytes
-// [lds + 16 i, lds + 16 i + 16). Issued from inline asm so that the compiler does not add
-// its own conservative waits on LDS reads; every wait on these copies is explicit
-// (wait_vmcnt) and so is the barrier. M0 (the LDS destination base) is written only by
-// these copies in this kernel, so the clobber of the reserved register is safe; the
-// compiler's note about it is silenced.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(unsigned voff, const char* base, unsigned lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(lds_wave_base), "s"(base)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Workgroup barrier that waits for this wave's LDS reads but not for its prefetches.
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Tile copies. Wave w copies rows 4w .. 4w+3 of the 32-row tile of K and of V (1 KB
 // apiece) into the ring slot at byte offset `slot`; lane i writes 16-byte slot i of that
@@ -181,39 +127,18 @@ __device__ __forceinline__ void load_tile(const Ctx& cx, int t) {
   load_tile_shifted(cx, t, (unsigned)(t & (kSlots - 1)) * kSlotBytes);
 }
 
-__device__ __forceinline__ bf16x8 lds_k(unsigned addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
-
-__device__ __forceinline__ bf16x8 lds_v_tr(unsigned a0, unsigned a1) {
-  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
-  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
-  u32x4 u;
-  u[0] = __builtin_bit_cast(u32x2, a)[0];
-  u[1] = __builtin_bit_cast(u32x2, a)[1];
-  u[2] = __builtin_bit_cast(u32x2, b)[0];
-  u[3] = __builtin_bit_cast(u32x2, b)[1];
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-// V operand i (key chunk kc = i / 4, d-block db = i % 4) of the tile in ring byte offset `slot`:
-// key half rd sits in 4-row block 4 kc + 2 rd + h32, d-block db at byte 256 db of the block.
-__device__ __forceinline__ bf16x8 v_operand(const Lane& ln, unsigned slot, int i) {
-  const int kc = i >> 2, db = i & 3;
-  const unsigned a = ln.vaddr + slot + 4096 * kc + 256 * db;
-  return lds_v_tr(a, a + 2048);
-}
-
 // S^T (32 keys x 32 queries) = K(slot) Q^T: 8 MFMAs over the 128 dims.
 __device__ __forceinline__ f32x16 qk_tile(unsigned slot, const bf16x8 (&qr)[8], const Lane& ln) {
   f32x16 S = {};
 #pragma unroll
-  for (int s = 0; s < 8; ++s) S = mfma(lds_k(ln.kaddr[s] + slot), qr[s], S);
+  for (int s = 0; s < 8; ++s) S = mfma(lds_row(ln.kaddr[s] + slot), qr[s], S);
   return S;
 }
 
 // O^T (128 dims x 32 queries) += V(slot)^T P^T: 2 key chunks of 16 x 4 d-blocks of 32.
 __device__ __forceinline__ void pv_tile(f32x16 (&O)[4], unsigned slot, const bf16x8 (&P)[2], const Lane& ln) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) O[i & 3] = mfma(v_operand(ln, slot, i), P[i >> 2], O[i & 3]);
+  for (int i = 0; i < 8; ++i) O[i & 3] = mfma(tr_operand(ln.vaddr, slot, i), P[i >> 2], O[i & 3]);
 }
 
 // Keys at and past `valid` in the tile are outside the segment: element v of S holds key
@@ -283,8 +208,8 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
   constexpr unsigned kslot = ((U + 1) % kSlots) * kSlotBytes;
   bf16x8 opnd[16];
   auto read = [&](int n) {
-    if (n < 8) opnd[n] = v_operand(ln, vslot, n);
-    else opnd[n] = lds_k(ln.kaddr[n - 8] + kslot);
+    if (n < 8) opnd[n] = tr_operand(ln.vaddr, vslot, n);
+    else opnd[n] = lds_row(ln.kaddr[n - 8] + kslot);
   };
   read(0);
   read(1);
@@ -470,10 +395,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   cx.vbase = (const char*)v + ((int64_t)seg_start * n_heads + head) * kRowBytes;
   {
     const int i = tid & 63;
-    cx.krow = 4 * wave + (i >> 4);
-    cx.koff = (unsigned)(((i & 15) ^ swz(cx.krow)) * 16);
-    cx.vrow = 4 * wave + ((i >> 2) & 3);
-    cx.voff = (unsigned)((4 * (i >> 4) + (i & 3)) * 16);
+    row_copy_lane(wave, i, cx.krow, cx.koff);  // K: row layout
+    tr_copy_lane(wave, i, cx.vrow, cx.voff);   // V: transposed-read layout
     cx.kconst = (unsigned)cx.krow * cx.row_stride + cx.koff;
     cx.vconst = (unsigned)cx.vrow * cx.row_stride + cx.voff;
   }
@@ -485,16 +408,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   ln.lane = tid & 63;
   ln.h32 = ln.lane >> 5;
   ln.l32 = ln.lane & 31;
-  {
-    const int sw = swz(ln.l32);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) ln.kaddr[s] = lds_base + ln.l32 * kRowBytes + ((((2 * s) | ln.h32) ^ sw) << 4);
-    // V^T operand (key chunk kc, d-block db, key half rd): lane i of 16-lane group
-    // (h32, g2) reads 8 bytes of row 16 kc + 8 rd + 4 h32 + i / 4, dims 32 db + 16 g2 +
-    // 4 (i % 4) .. +3, i.e. chunk 4 db + 2 g2 + (i % 4) / 2 of 4-row block 4 kc + 2 rd + h32.
-    const int i = ln.lane & 15, g2 = (ln.lane >> 4) & 1;
-    ln.vaddr = lds_base + kRingBytes + 1024 * ln.h32 + 16 * (4 * (i >> 2) + 2 * g2 + ((i & 3) >> 1)) + 8 * (i & 1);
-  }
+  for (int s = 0; s < 8; ++s) ln.kaddr[s] = row_read_addr(lds_base, ln.l32, ln.h32, s);
+  ln.vaddr = tr_read_base(lds_base + kRingBytes, ln.lane);
 
   // Q^T operand: lane holds q[row][16 s + 8 h32 .. +7] for s = 0..7.
   bf16x8 qr[8];

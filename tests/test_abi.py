@@ -116,3 +116,40 @@ def test_prologue_validation_before_any_hip_call(args, code):
     rc = lsv.lsv_qkv_prologue(a["q"], a["k"], a["v"], a["q_weight"], a["k_weight"], a["cos"], a["sin"], a["out"],
                               a["batch"], a["seq_len"], a["n_heads"], a["head_dim"], a["rotary_dim"], a["eps"], None)
     assert rc == code
+
+
+def test_bwd_workspace_size():
+    assert lsv.lsv_attn_bwd_workspace_size(161394, 56) == 8 * 161394 * 56
+    assert lsv.lsv_attn_bwd_workspace_size(0, 4) == 0
+    assert lsv.lsv_attn_bwd_workspace_size(-1, 4) == -1
+    assert lsv.lsv_attn_bwd_workspace_size(10, 0) == -1
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_seqs=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(o=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dout=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dk=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(ws=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(ws_bytes=8 * 10 * 4 - 1), lsv.LSV_ERR_INVALID_ARG),   # one byte short
+    (dict(dv=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(dout=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(ws=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(total_tokens=1 << 31, ws_bytes=1 << 40), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(total_tokens=40_000_000, n_heads=56, ws_bytes=1 << 40), lsv.LSV_ERR_UNSUPPORTED),  # T*H >= 2^31
+    (dict(max_seqlen=299_594, total_tokens=299_594, n_heads=56, ws_bytes=1 << 40), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(n_seqs=0), lsv.LSV_OK),
+    (dict(max_seqlen=0, ws=0), lsv.LSV_OK),
+])
+def test_bwd_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, cu=A, n_seqs=1, max_seqlen=10, total_tokens=10,
+             n_heads=4, head_dim=128, scale=0.125, ws=A, ws_bytes=8 * 10 * 4)
+    a.update(args)
+    rc = lsv.lsv_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"], a["cu"],
+                          a["n_seqs"], a["max_seqlen"], a["total_tokens"], a["n_heads"], a["head_dim"], a["scale"],
+                          a["ws"], a["ws_bytes"], None)
+    assert rc == code
