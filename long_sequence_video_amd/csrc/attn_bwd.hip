@@ -8,13 +8,16 @@
 //   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i,   dV_j = sum_i P_ij dO_i.
 //
 // Design (gfx950, wave64), three kernels on the caller's stream, no atomics (deterministic):
-//  * prep: D and -LSE log2(e) per (head, token) into the workspace (16 lanes per row, like
-//    the other row-streaming passes).
+//  * prep: -LSE / scale and -D per (head, token) into the workspace (16 lanes per row, like
+//    the other row-streaming passes). In raw score units, P = exp2(log2(e) scale (s - LSE /
+//    scale)), so the dK/dV kernel starts its S accumulator at -LSE / scale and its dP
+//    accumulator at -D: the products come out as s - LSE / scale and dP - D, and each
+//    element then costs one multiply and one exp2 for P and one multiply for dS.
 //  * dK/dV: one workgroup = 8 waves = 256 keys of one (segment, head); each wave owns 32 keys
 //    with K and V held in registers as MFMA B operands. Query tiles of 32 rows stream through
 //    a 4-slot LDS ring, each stored twice: in the row layout (A operand of S = Q K^T and
 //    dP = dO V^T) and in the transposed-read layout (A operand of dK^T += Q^T dS and
-//    dV^T += dO^T P), plus the tile's -LSE log2(e) and D. The S and dP accumulators give a
+//    dV^T += dO^T P), plus the tile's -LSE / scale and -D. The S and dP accumulators give a
 //    lane one key and 16 queries; P and dS converted to bf16 are the B operands of the two
 //    accumulating products as they are.
 //  * dQ: one workgroup = 256 queries; K and V tiles of 32 keys stream through the ring (K in
@@ -42,14 +45,13 @@ constexpr int kBT = kTileRows;            // rows per streamed tile
 constexpr int kSlots = 4;                 // ring slots
 constexpr int kAhead = 3;                 // tiles in flight ahead of use
 constexpr int kRing = kSlots * kTileBytes;  // one region of the ring: 32 KB
-constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kAhead <= kSlots - 1, "a slot is reloaded only after every wave has left it");
 
 // dQ kernel LDS: K rows | V rows | K transposed-read, one 32 KB ring region each.
 constexpr int kDqLds = 3 * kRing;
 constexpr int kDqOps = 3;                 // copies per wave per tile
-// dK/dV kernel LDS: Q rows | dO rows | Q transposed | dO transposed | stats (nl, D).
-constexpr int kStatBytes = 2 * kBT * 4;   // 32 floats of -LSE log2(e), 32 of D
+// dK/dV kernel LDS: Q rows | dO rows | Q transposed | dO transposed | stats.
+constexpr int kStatBytes = 2 * kBT * 4;   // 32 floats of -LSE / scale, 32 of -D
 constexpr int kDkvLds = 4 * kRing + kSlots * kStatBytes;
 constexpr int kDkvOps = 5;
 
@@ -123,7 +125,7 @@ __device__ __forceinline__ int tile_start(int t, int seg_len) { return min(t * k
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const u32x4* __restrict__ o, const u32x4* __restrict__ dout, const float* __restrict__ lse,
                 float* __restrict__ ws_nl, float* __restrict__ ws_d, unsigned n_rows, unsigned n_heads,
-                int64_t total_tokens) {
+                int64_t total_tokens, float inv_scale) {
   const int j = threadIdx.x & 15;
   const unsigned stride = gridDim.x * 16;
   for (unsigned row = blockIdx.x * 16 + (threadIdx.x >> 4); row < n_rows; row += stride) {
@@ -142,8 +144,8 @@ bwd_prep_kernel(const u32x4* __restrict__ o, const u32x4* __restrict__ dout, con
     if (j == 0) {
       const unsigned t = row / n_heads, h = row % n_heads;
       const int64_t s = (int64_t)h * total_tokens + t;
-      ws_d[s] = acc;
-      ws_nl[s] = -lse[s] * kLog2e;
+      ws_d[s] = -acc;                   // -D
+      ws_nl[s] = -lse[s] * inv_scale;  // -LSE / scale
     }
   }
 }
@@ -161,21 +163,22 @@ struct DqCtx {
   unsigned rconst, tconst;  // rrow * row_stride + roff, trow * row_stride + toff
 };
 
+// Segments of 32 keys or more: tile t is rows tile_start(t) .. +31 (uniform offset).
 __device__ __forceinline__ void dq_load(const DqCtx& cx, int t) {
-  const unsigned slot = (unsigned)(t & (kSlots - 1)) * kTileBytes;
-  const unsigned lds = cx.lds_copy + slot;
-  if (cx.seg_len >= kBT) {
-    const unsigned off = (unsigned)tile_start(t, cx.seg_len) * cx.row_stride;
-    dma16(cx.rconst, cx.kbase + off, lds);
-    dma16(cx.rconst, cx.vbase + off, lds + kRing);
-    dma16(cx.tconst, cx.kbase + off, lds + 2 * kRing);
-  } else {  // a single tile shorter than 32 keys: rows past the segment repeat its last row
-    const int last = cx.seg_len - 1;
-    const unsigned r = (unsigned)min(cx.rrow, last), tr = (unsigned)min(cx.trow, last);
-    dma16(__umul24(r, cx.row_stride) + cx.roff, cx.kbase, lds);
-    dma16(__umul24(r, cx.row_stride) + cx.roff, cx.vbase, lds + kRing);
-    dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.kbase, lds + 2 * kRing);
-  }
+  const unsigned lds = cx.lds_copy + (unsigned)(t & (kSlots - 1)) * kTileBytes;
+  const unsigned off = (unsigned)tile_start(t, cx.seg_len) * cx.row_stride;
+  dma16(cx.rconst, cx.kbase + off, lds);
+  dma16(cx.rconst, cx.vbase + off, lds + kRing);
+  dma16(cx.tconst, cx.kbase + off, lds + 2 * kRing);
+}
+
+// A single tile shorter than 32 keys (slot 0): rows past the segment repeat its last row.
+__device__ __forceinline__ void dq_load_short(const DqCtx& cx) {
+  const unsigned last = (unsigned)cx.seg_len - 1;
+  const unsigned r = min((unsigned)cx.rrow, last), tr = min((unsigned)cx.trow, last);
+  dma16(__umul24(r, cx.row_stride) + cx.roff, cx.kbase, cx.lds_copy);
+  dma16(__umul24(r, cx.row_stride) + cx.roff, cx.vbase, cx.lds_copy + kRing);
+  dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.kbase, cx.lds_copy + 2 * kRing);
 }
 
 struct DqLane {
@@ -190,7 +193,7 @@ __device__ __forceinline__ void dq_step(const DqCtx& cx, const DqLane& ln, int t
   constexpr unsigned slot = U * kTileBytes;
   wait_vmcnt<kDqOps * (kAhead - 1)>();
   barrier_lds();
-  dq_load(cx, t + kAhead);
+  if (n_t > 1) dq_load(cx, t + kAhead);  // a single-tile segment needs no prefetch
   f32x16 S = {}, dP = {};
 #pragma unroll
   for (int s = 0; s < 8; ++s) S = mfma(lds_row(ln.raddr[s] + slot), qr[s], S);
@@ -205,7 +208,7 @@ __device__ __forceinline__ void dq_step(const DqCtx& cx, const DqLane& ln, int t
   for (int j = 0; j < 8; ++j) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * j], c, nl));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * j + 1], c, nl));
-    pack_pair(ds, j, p0 * (dP[2 * j] - dd), p1 * (dP[2 * j + 1] - dd));
+    pack_pair(ds, j, p0 * (dP[2 * j] + dd), p1 * (dP[2 * j + 1] + dd));
   }
   const bf16x8 dsb[2] = {__builtin_bit_cast(bf16x8, ds[0]), __builtin_bit_cast(bf16x8, ds[1])};
 #pragma unroll
@@ -257,15 +260,19 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       dor[s] = *(const bf16x8*)(dout + off + 16 * s);
     }
   }
-  const float nl = ws_nl[(int64_t)w.head * total_tokens + tok];
-  const float dd = ws_d[(int64_t)w.head * total_tokens + tok];
+  const float nl = c * ws_nl[(int64_t)w.head * total_tokens + tok];  // -LSE log2(e)
+  const float dd = ws_d[(int64_t)w.head * total_tokens + tok];        // -D
 
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
   const int n_t = (w.seg_len + kBT - 1) / kBT;
+  if (w.seg_len >= kBT) {
 #pragma unroll
-  for (int t = 0; t < kAhead; ++t) dq_load(cx, t);
+    for (int t = 0; t < kAhead; ++t) dq_load(cx, t);
+  } else {
+    dq_load_short(cx);  // fewer copies in flight than the waits allow: they return early
+  }
   for (int t = 0; t < n_t; t += kSlots) {
     dq_step<0>(cx, ln, t, n_t, qr, dor, nl, dd, c, acc);
     if (t + 1 < n_t) dq_step<1>(cx, ln, t + 1, n_t, qr, dor, nl, dd, c, acc);
@@ -309,27 +316,28 @@ struct KvCtx {
   int stat_row;         // row of this lane's stats float
 };
 
+// Segments of 32 queries or more: tile t is rows tile_start(t) .. +31 (uniform offset).
 __device__ __forceinline__ void kv_load(const KvCtx& cx, int t, int lane) {
-  const unsigned slot = (unsigned)(t & (kSlots - 1)) * kTileBytes;
-  const unsigned lds = cx.lds_copy + slot;
+  const unsigned lds = cx.lds_copy + (unsigned)(t & (kSlots - 1)) * kTileBytes;
   const unsigned lstat = cx.lds_stat + (unsigned)(t & (kSlots - 1)) * kStatBytes;
-  if (cx.seg_len >= kBT) {
-    const int start = tile_start(t, cx.seg_len);
-    const unsigned off = (unsigned)start * cx.row_stride;
-    dma16(cx.rconst, cx.qbase + off, lds);
-    dma16(cx.rconst, cx.dobase + off, lds + kRing);
-    dma16(cx.tconst, cx.qbase + off, lds + 2 * kRing);
-    dma16(cx.tconst, cx.dobase + off, lds + 3 * kRing);
-    if (lane < 8) dma4(cx.stat_off, cx.statbase + 4 * start, lstat);  // one copy per wave, 8 lanes
-  } else {
-    const int last = cx.seg_len - 1;
-    const unsigned r = (unsigned)min(cx.rrow, last), tr = (unsigned)min(cx.trow, last);
-    dma16(__umul24(r, cx.row_stride) + cx.roff, cx.qbase, lds);
-    dma16(__umul24(r, cx.row_stride) + cx.roff, cx.dobase, lds + kRing);
-    dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.qbase, lds + 2 * kRing);
-    dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.dobase, lds + 3 * kRing);
-    if (lane < 8) dma4(4u * (unsigned)min(cx.stat_row, last), cx.statbase, lstat);
-  }
+  const int start = tile_start(t, cx.seg_len);
+  const unsigned off = (unsigned)start * cx.row_stride;
+  dma16(cx.rconst, cx.qbase + off, lds);
+  dma16(cx.rconst, cx.dobase + off, lds + kRing);
+  dma16(cx.tconst, cx.qbase + off, lds + 2 * kRing);
+  dma16(cx.tconst, cx.dobase + off, lds + 3 * kRing);
+  if (lane < 8) dma4(cx.stat_off, cx.statbase + 4 * start, lstat);  // one copy per wave, 8 lanes
+}
+
+// A single tile shorter than 32 queries (slot 0): rows past the segment repeat its last row.
+__device__ __forceinline__ void kv_load_short(const KvCtx& cx, int lane) {
+  const unsigned last = (unsigned)cx.seg_len - 1;
+  const unsigned r = min((unsigned)cx.rrow, last), tr = min((unsigned)cx.trow, last);
+  dma16(__umul24(r, cx.row_stride) + cx.roff, cx.qbase, cx.lds_copy);
+  dma16(__umul24(r, cx.row_stride) + cx.roff, cx.dobase, cx.lds_copy + kRing);
+  dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.qbase, cx.lds_copy + 2 * kRing);
+  dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.dobase, cx.lds_copy + 3 * kRing);
+  if (lane < 8) dma4(4u * min((unsigned)cx.stat_row, last), cx.statbase, cx.lds_stat);
 }
 
 struct KvLane {
@@ -347,9 +355,20 @@ __device__ __forceinline__ void kv_step(const KvCtx& cx, const KvLane& ln, int t
   constexpr unsigned sslot = U * kStatBytes;
   wait_vmcnt<kDkvOps * (kAhead - 1)>();
   barrier_lds();
-  kv_load(cx, t + kAhead, ln.lane);
-  // S = Q K^T and dP = dO V^T: lane = key l32, element v = query 8 (v / 4) + 4 h32 + v % 4.
-  f32x16 S = {}, dP = {};
+  if (n_t > 1) kv_load(cx, t + kAhead, ln.lane);  // a single-tile segment needs no prefetch
+  // S = Q K^T - LSE / scale and dP = dO V^T - D: lane = key l32, element v = query
+  // 8 (v / 4) + 4 h32 + v % 4, whose stats are the 4 consecutive floats at 8 (v / 4) + 4 h32.
+  f32x16 S, dP;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const f32x4 ls = *(lds_f32x4*)(uintptr_t)(ln.staddr + sslot + 32 * a);
+    const f32x4 nd = *(lds_f32x4*)(uintptr_t)(ln.staddr + sslot + 32 * a + kBT * 4);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      S[4 * a + b] = ls[b];
+      dP[4 * a + b] = nd[b];
+    }
+  }
 #pragma unroll
   for (int s = 0; s < 8; ++s) S = mfma(lds_row(ln.raddr[s] + slot), kr[s], S);
 #pragma unroll
@@ -358,20 +377,14 @@ __device__ __forceinline__ void kv_step(const KvCtx& cx, const KvLane& ln, int t
     if (cx.seg_len >= kBT) mask_head(S, kBT * n_t - cx.seg_len, ln.h32);
     else mask_tail(S, cx.seg_len, ln.h32);
   }
-  f32x4 nl[4], dd[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    nl[a] = *(lds_f32x4*)(uintptr_t)(ln.staddr + sslot + 32 * a);
-    dd[a] = *(lds_f32x4*)(uintptr_t)(ln.staddr + sslot + 32 * a + kBT * 4);
-  }
   u32x4 pb[2], sb[2];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int v0 = 2 * j, v1 = 2 * j + 1;
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[v0], c, nl[v0 >> 2][v0 & 3]));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[v1], c, nl[v1 >> 2][v1 & 3]));
+    const float p0 = __builtin_amdgcn_exp2f(S[v0] * c);
+    const float p1 = __builtin_amdgcn_exp2f(S[v1] * c);
     pack_pair(pb, j, p0, p1);
-    pack_pair(sb, j, p0 * (dP[v0] - dd[v0 >> 2][v0 & 3]), p1 * (dP[v1] - dd[v1 >> 2][v1 & 3]));
+    pack_pair(sb, j, p0 * dP[v0], p1 * dP[v1]);
   }
   const bf16x8 P[2] = {__builtin_bit_cast(bf16x8, pb[0]), __builtin_bit_cast(bf16x8, pb[1])};
   const bf16x8 dS[2] = {__builtin_bit_cast(bf16x8, sb[0]), __builtin_bit_cast(bf16x8, sb[1])};
@@ -418,7 +431,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   cx.dbase = (const char*)(ws_d + (int64_t)w.head * total_tokens + w.seg_start);
   cx.seg_len = w.seg_len;
   cx.lds_copy = lds_base + wave * 1024;
-  // Stats: waves 0..3 copy -LSE log2 e, waves 4..7 copy D; wave w's 8 lanes copy floats
+  // Stats: waves 0..3 copy -LSE / scale, waves 4..7 copy -D; wave w's 8 lanes copy floats
   // 8 (w % 4) .. +7 of the tile.
   cx.statbase = wave < 4 ? cx.nlbase : cx.dbase;
   cx.lds_stat = lds_base + 4 * kRing + (wave < 4 ? 0 : kBT * 4) + 32 * (wave & 3);
@@ -460,8 +473,12 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     dva[db] = f32x16{};
   }
   const int n_t = (w.seg_len + kBT - 1) / kBT;
+  if (w.seg_len >= kBT) {
 #pragma unroll
-  for (int t = 0; t < kAhead; ++t) kv_load(cx, t, lane);
+    for (int t = 0; t < kAhead; ++t) kv_load(cx, t, lane);
+  } else {
+    kv_load_short(cx, lane);
+  }
   for (int t = 0; t < n_t; t += kSlots) {
     kv_step<0>(cx, ln, t, n_t, kr, vr, c, dka, dva);
     if (t + 1 < n_t) kv_step<1>(cx, ln, t + 1, n_t, kr, vr, c, dka, dva);
@@ -524,7 +541,8 @@ int lsv_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   const int64_t prep_grid = prep_need < (1 << 22) ? prep_need : (1 << 22);
   (void)hipGetLastError();
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)prep_grid), dim3(256), 0, st, (const u32x4*)o,
-                     (const u32x4*)dout, lse, ws_nl, ws_d, (unsigned)rows, (unsigned)n_heads, total_tokens);
+                     (const u32x4*)dout, lse, ws_nl, ws_d, (unsigned)rows, (unsigned)n_heads, total_tokens,
+                     (float)(1.0 / (double)scale));
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)grid), dim3(kThreads), kDkvLds, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws_nl, ws_d, (uint16_t*)dk,
                      (uint16_t*)dv, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens,
