@@ -189,27 +189,33 @@ struct DqLane {
 
 template <int U>
 __device__ __forceinline__ void dq_step(const DqCtx& cx, const DqLane& ln, int t, int n_t, const bf16x8 (&qr)[8],
-                                        const bf16x8 (&dor)[8], float nl, float dd, float c, f32x16 (&acc)[4]) {
+                                        const bf16x8 (&dor)[8], float nl, const f32x16& dinit, float c,
+                                        f32x16 (&acc)[4]) {
   constexpr unsigned slot = U * kTileBytes;
   wait_vmcnt<kDqOps * (kAhead - 1)>();
   barrier_lds();
   if (n_t > 1) dq_load(cx, t + kAhead);  // a single-tile segment needs no prefetch
-  f32x16 S = {}, dP = {};
+  // S^T first; then the dP^T chain (started at -D) with the exp2 work of P placed between its
+  // MFMAs; dS needs the finished dP^T.
+  f32x16 S = {}, dP = dinit;
 #pragma unroll
   for (int s = 0; s < 8; ++s) S = mfma(lds_row(ln.raddr[s] + slot), qr[s], S);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) dP = mfma(lds_row(ln.raddr[s] + slot + kRing), dor[s], dP);
+  sched_fence();
   if (t == n_t - 1) {
     if (cx.seg_len >= kBT) mask_head(S, kBT * n_t - cx.seg_len, ln.h32);
     else mask_tail(S, cx.seg_len, ln.h32);
   }
+  float p[16];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    dP = mfma(lds_row(ln.raddr[s] + slot + kRing), dor[s], dP);
+    p[2 * s] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * s], c, nl));
+    p[2 * s + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * s + 1], c, nl));
+    sched_fence();
+  }
   u32x4 ds[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * j], c, nl));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * j + 1], c, nl));
-    pack_pair(ds, j, p0 * (dP[2 * j] + dd), p1 * (dP[2 * j + 1] + dd));
-  }
+  for (int j = 0; j < 8; ++j) pack_pair(ds, j, p[2 * j] * dP[2 * j], p[2 * j + 1] * dP[2 * j + 1]);
   const bf16x8 dsb[2] = {__builtin_bit_cast(bf16x8, ds[0]), __builtin_bit_cast(bf16x8, ds[1])};
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i & 3] = mfma(tr_operand(ln.taddr, slot, i), dsb[i >> 2], acc[i & 3]);
@@ -261,7 +267,12 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   }
   const float nl = c * ws_nl[(int64_t)w.head * total_tokens + tok];  // -LSE log2(e)
-  const float dd = ws_d[(int64_t)w.head * total_tokens + tok];        // -D
+  f32x16 dinit;  // -D in every element: the starting value of each tile's dP^T
+  {
+    const float nd = ws_d[(int64_t)w.head * total_tokens + tok];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dinit[e] = nd;
+  }
 
   f32x16 acc[4];
 #pragma unroll
@@ -274,10 +285,10 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     dq_load_short(cx);  // fewer copies in flight than the waits allow: they return early
   }
   for (int t = 0; t < n_t; t += kSlots) {
-    dq_step<0>(cx, ln, t, n_t, qr, dor, nl, dd, c, acc);
-    if (t + 1 < n_t) dq_step<1>(cx, ln, t + 1, n_t, qr, dor, nl, dd, c, acc);
-    if (t + 2 < n_t) dq_step<2>(cx, ln, t + 2, n_t, qr, dor, nl, dd, c, acc);
-    if (t + 3 < n_t) dq_step<3>(cx, ln, t + 3, n_t, qr, dor, nl, dd, c, acc);
+    dq_step<0>(cx, ln, t, n_t, qr, dor, nl, dinit, c, acc);
+    if (t + 1 < n_t) dq_step<1>(cx, ln, t + 1, n_t, qr, dor, nl, dinit, c, acc);
+    if (t + 2 < n_t) dq_step<2>(cx, ln, t + 2, n_t, qr, dor, nl, dinit, c, acc);
+    if (t + 3 < n_t) dq_step<3>(cx, ln, t + 3, n_t, qr, dor, nl, dinit, c, acc);
   }
   wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS when it exits
 
@@ -309,8 +320,7 @@ struct KvCtx {
   int seg_len;
   unsigned lds_copy;    // this wave's 1 KB block in slot 0 of ring region 0
   unsigned lds_stat;    // this wave's 32-byte block in stats slot 0
-  const char* statbase; // nlbase or dbase, by wave
-  unsigned stat_off;    // lane byte offset inside the 32-float tile (lanes 0..7)
+  const char* statbase; // nlbase or dbase, by wave, plus this wave's 8 floats (uniform)
   int rrow, trow;
   unsigned roff, toff, rconst, tconst;
   int stat_row;         // row of this lane's stats float
@@ -326,18 +336,23 @@ __device__ __forceinline__ void kv_load(const KvCtx& cx, int t, int lane) {
   dma16(cx.rconst, cx.dobase + off, lds + kRing);
   dma16(cx.tconst, cx.qbase + off, lds + 2 * kRing);
   dma16(cx.tconst, cx.dobase + off, lds + 3 * kRing);
-  if (lane < 8) dma4(cx.stat_off, cx.statbase + 4 * start, lstat);  // one copy per wave, 8 lanes
+  // One stats copy per wave, lanes 0..7. The lane offset is recomputed here (lane id from
+  // v_mbcnt, in a volatile statement the compiler cannot hoist): a register held across the
+  // loop would be spilled, and its reload would make the compiler drain every prefetch.
+  unsigned lid;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(lid));
+  if (lane < 8) dma4(lid * 4u, cx.statbase + 4 * start, lstat);
 }
 
 // A single tile shorter than 32 queries (slot 0): rows past the segment repeat its last row.
-__device__ __forceinline__ void kv_load_short(const KvCtx& cx, int lane) {
+__device__ __forceinline__ void kv_load_short(const KvCtx& cx, int lane, int wave) {
   const unsigned last = (unsigned)cx.seg_len - 1;
   const unsigned r = min((unsigned)cx.rrow, last), tr = min((unsigned)cx.trow, last);
   dma16(__umul24(r, cx.row_stride) + cx.roff, cx.qbase, cx.lds_copy);
   dma16(__umul24(r, cx.row_stride) + cx.roff, cx.dobase, cx.lds_copy + kRing);
   dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.qbase, cx.lds_copy + 2 * kRing);
   dma16(__umul24(tr, cx.row_stride) + cx.toff, cx.dobase, cx.lds_copy + 3 * kRing);
-  if (lane < 8) dma4(4u * min((unsigned)cx.stat_row, last), cx.statbase, cx.lds_stat);
+  if (lane < 8) dma4(4u * min((unsigned)cx.stat_row, last), cx.statbase - 32 * (wave & 3), cx.lds_stat);
 }
 
 struct KvLane {
@@ -369,27 +384,34 @@ __device__ __forceinline__ void kv_step(const KvCtx& cx, const KvLane& ln, int t
       dP[4 * a + b] = nd[b];
     }
   }
+  // S first; then the dP chain with P's exp2 work placed between its MFMAs; then dV with
+  // dS's work between its MFMAs; then dK. Scheduling barriers hold this order, so each
+  // wave keeps the matrix pipe fed while its vector ALU works.
 #pragma unroll
   for (int s = 0; s < 8; ++s) S = mfma(lds_row(ln.raddr[s] + slot), kr[s], S);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) dP = mfma(lds_row(ln.raddr[s] + slot + kRing), vr[s], dP);
+  sched_fence();
   if (t == n_t - 1) {
     if (cx.seg_len >= kBT) mask_head(S, kBT * n_t - cx.seg_len, ln.h32);
     else mask_tail(S, cx.seg_len, ln.h32);
   }
+  // P and dS are formed in place of S and dP (fewer live registers).
   u32x4 pb[2], sb[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int v0 = 2 * j, v1 = 2 * j + 1;
-    const float p0 = __builtin_amdgcn_exp2f(S[v0] * c);
-    const float p1 = __builtin_amdgcn_exp2f(S[v1] * c);
-    pack_pair(pb, j, p0, p1);
-    pack_pair(sb, j, p0 * dP[v0], p1 * dP[v1]);
+  for (int s = 0; s < 8; ++s) {
+    dP = mfma(lds_row(ln.raddr[s] + slot + kRing), vr[s], dP);
+    S[2 * s] = __builtin_amdgcn_exp2f(S[2 * s] * c);
+    S[2 * s + 1] = __builtin_amdgcn_exp2f(S[2 * s + 1] * c);
+    pack_pair(pb, s, S[2 * s], S[2 * s + 1]);
+    sched_fence();
   }
   const bf16x8 P[2] = {__builtin_bit_cast(bf16x8, pb[0]), __builtin_bit_cast(bf16x8, pb[1])};
-  const bf16x8 dS[2] = {__builtin_bit_cast(bf16x8, sb[0]), __builtin_bit_cast(bf16x8, sb[1])};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dv[i & 3] = mfma(tr_operand(ln.dotaddr, slot, i), P[i >> 2], dv[i & 3]);
+  for (int i = 0; i < 8; ++i) {
+    dv[i & 3] = mfma(tr_operand(ln.dotaddr, slot, i), P[i >> 2], dv[i & 3]);
+    pack_pair(sb, i, S[2 * i] * dP[2 * i], S[2 * i + 1] * dP[2 * i + 1]);
+    sched_fence();
+  }
+  const bf16x8 dS[2] = {__builtin_bit_cast(bf16x8, sb[0]), __builtin_bit_cast(bf16x8, sb[1])};
 #pragma unroll
   for (int i = 0; i < 8; ++i) dk[i & 3] = mfma(tr_operand(ln.qtaddr, slot, i), dS[i >> 2], dk[i & 3]);
 }
@@ -433,10 +455,9 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   cx.lds_copy = lds_base + wave * 1024;
   // Stats: waves 0..3 copy -LSE / scale, waves 4..7 copy -D; wave w's 8 lanes copy floats
   // 8 (w % 4) .. +7 of the tile.
-  cx.statbase = wave < 4 ? cx.nlbase : cx.dbase;
+  cx.statbase = (wave < 4 ? cx.nlbase : cx.dbase) + 32 * (wave & 3);  // floats 8 (w % 4) ..
   cx.lds_stat = lds_base + 4 * kRing + (wave < 4 ? 0 : kBT * 4) + 32 * (wave & 3);
   cx.stat_row = 8 * (wave & 3) + (lane & 7);
-  cx.stat_off = 4u * (unsigned)cx.stat_row;
   row_copy_lane(wave, lane, cx.rrow, cx.roff);
   tr_copy_lane(wave, lane, cx.trow, cx.toff);
   cx.rconst = (unsigned)cx.rrow * cx.row_stride + cx.roff;
@@ -477,7 +498,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) kv_load(cx, t, lane);
   } else {
-    kv_load_short(cx, lane);
+    kv_load_short(cx, lane, wave);
   }
   for (int t = 0; t < n_t; t += kSlots) {
     kv_step<0>(cx, ln, t, n_t, kr, vr, c, dka, dva);
