@@ -33,7 +33,7 @@ Sources (the pages):
     and SM107", Description: the transformer blocks run non-causal BF16
     attention at the packed clip length (19k to 104k tokens, 56 heads x 128).
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
   * LSE is the natural log of the sum of exponentials of the *scaled* logits
     (the FlashAttention convention); the pages never state the base.
   * ``sigma`` is the fp32 value handed to the kernel, widened exactly to fp64.

@@ -23,7 +23,7 @@ V (the kernel writes plane 0, 1, 2; the page's int32-plane test checks
 ``out[2B:] == v``). The kernel computes in fp32 and rounds once to bf16; this
 oracle keeps the unrounded fp64 value.
 
-Readings where the page is terse (also listed in the design notes):
+Readings where the page is terse:
   * ``eps`` is the fp32 value handed to the kernel (1e-5 for the H3 blocks),
     widened exactly.
   * Tables and weights are bf16 (the page's wrapper casts cos/sin to the
