@@ -307,3 +307,83 @@ def make_prologue_config(name: str) -> PrologueInputs:
     if name not in PROLOGUE_CONFIGS:
         raise KeyError(f"unknown prologue workload {name!r}; known: {sorted(PROLOGUE_CONFIGS)}")
     return generate_prologue(name=name, **PROLOGUE_CONFIGS[name])
+
+
+# ---------------------------------------------------------------- FP8 (e4m3) attention inputs
+
+E4M3_MAX = 448.0
+
+
+def f64_to_e4m3_bits(x) -> np.ndarray:
+    """Quantise to OCP FP8 e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+    infinities): round to nearest even, subnormals below 2^-6, saturation at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (x < 0) | ((x == 0) & np.signbit(x))
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    q = 2.0 ** (e - 3)                       # spacing of the binade (subnormals: 2^-9)
+    r = np.minimum(np.round(a / q) * q, E4M3_MAX)   # numpy rounds half to even
+    # encode r exactly
+    ee = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    normal = r >= 2.0 ** -6
+    exp_field = np.where(normal, ee + 7, 0).astype(np.int64)
+    mant = np.where(normal, r / 2.0 ** ee - 1.0, r / 2.0 ** -9 / 8.0) * 8.0
+    mant = np.rint(mant).astype(np.int64)
+    bits = (exp_field << 3) | mant
+    bits = np.where(r == 0, 0, bits)
+    return (bits | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+@dataclass
+class Fp8Inputs:
+    """One FP8 attention workload: e4m3 q/k/v bytes with per-tensor descales (fp32)."""
+    name: str
+    q: np.ndarray           # uint8 [total, heads, head_dim]
+    k: np.ndarray
+    v: np.ndarray
+    descale_q: float
+    descale_k: float
+    descale_v: float
+    cu_seqlens: np.ndarray
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def n_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def seqlens(self) -> list[int]:
+        cu = self.cu_seqlens.astype(np.int64)
+        return [int(b - a) for a, b in zip(cu[:-1], cu[1:])]
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.seqlens, default=0)
+
+    def flops(self) -> float:
+        return float(sum(4.0 * s * s * self.n_heads * self.q.shape[2] for s in self.seqlens))
+
+
+def quantize_fp8(inp: Inputs, name: str | None = None) -> Fp8Inputs:
+    """Per-tensor e4m3 quantisation of a bf16 workload: descale = fp32(amax / 448), values
+    x / descale rounded to e4m3 (the usual amax recipe for FP8 attention inputs)."""
+    out = {}
+    for key in ("q", "k", "v"):
+        bits = getattr(inp, key)
+        xf = (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        amax = float(np.abs(xf).max()) or 1.0
+        d = float(np.float32(amax / E4M3_MAX))
+        out[key] = (f64_to_e4m3_bits(xf / d), d)
+    return Fp8Inputs(name or inp.name + "_fp8", out["q"][0], out["k"][0], out["v"][0], out["q"][1], out["k"][1],
+                     out["v"][1], inp.cu_seqlens, inp.scale, dict(inp.meta))
+
+
+def make_fp8_config(name: str) -> Fp8Inputs:
+    """The FP8 version of a named workload (same seeds and structure, quantised per tensor)."""
+    return quantize_fp8(make_config(name), name + "_fp8")
