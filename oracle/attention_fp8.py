@@ -30,8 +30,8 @@ from .attention import f32_to_f64, segments
 __all__ = ["e4m3_bits_to_f64", "attention_fp8_fp64"]
 
 
-def e4m3_bits_to_f64(bits) -> np.ndarray:
-    """Exact value of e4m3 bytes (NaN for the two NaN codes)."""
+def _decode_fields(bits) -> np.ndarray:
+    """The format's definition, field by field."""
     b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
     sign = np.where(b & 0x80, -1.0, 1.0)
     e = (b >> 3) & 0xF
@@ -39,6 +39,14 @@ def e4m3_bits_to_f64(bits) -> np.ndarray:
     val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
     val = np.where((e == 0xF) & (m == 0x7), np.nan, val)
     return sign * val
+
+
+_TABLE = _decode_fields(np.arange(256, dtype=np.uint8))  # all 256 codes, by the definition
+
+
+def e4m3_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of e4m3 bytes (NaN for the two NaN codes): the definition, tabulated."""
+    return _TABLE[np.asarray(bits, dtype=np.uint8)]
 
 
 def attention_fp8_fp64(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, cu_seqlens,
