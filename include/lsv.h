@@ -1,5 +1,5 @@
-/* lsv: dense non-causal varlen BF16 attention forward and backward for AMD MI355X (gfx950),
- * and the fused QKV prologue (QK RMSNorm + partial RoPE) that feeds them.
+/* lsv: dense non-causal varlen attention for AMD MI355X (gfx950): the BF16 forward and backward,
+ * an FP8 (e4m3) forward, and the fused QKV prologue (QK RMSNorm + partial RoPE) that feeds them.
  *
  * The operation (FastVideo #2049, diff of fastvideo/attention/utils/flash_attn_cute.py,
  * the varlen forward wrapper; TensorRT-LLM PR #21275, Description): for every packed
@@ -64,6 +64,28 @@ enum lsv_status {
 int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
                  float scale, void* stream);
+
+/* FP8 (e4m3) attention forward on the caller's stream (asynchronous).
+ *
+ * The operation (TensorRT-LLM PR #21275, the MiniMax-H3 recipe commit: attention with
+ * --qk-dtype fp8 --v-dtype fp8 and per-tensor FP8 descales, the LSE returned; over the varlen
+ * forward of FastVideo #2049): q, k, v hold OCP FP8 e4m3 bytes (sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities) whose real values are descale_x * x8; then, as for
+ * lsv_attn_fwd,
+ *     z_ij = scale * (descale_q q8_i) . (descale_k k8_j),   O_i = sum_j softmax_j(z_ij) descale_v v8_j,
+ *     LSE_i = ln sum_j exp(z_ij).
+ * The attention weights are rounded to e4m3 for the P.V product and O is normalised by the sum
+ * of those rounded weights; the LSE uses the fp32 weights. O is bf16, LSE fp32.
+ *
+ * q, k, v      device pointers, uint8 e4m3 [total_tokens, n_heads, head_dim], 16-byte aligned.
+ * descale_q, descale_k, descale_v  finite, > 0.
+ * o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale, stream:
+ *              as for lsv_attn_fwd (same layouts, limits and skipped-segment rule; the 32-bit
+ *              offset limit is max_seqlen * n_heads * head_dim + head_dim < 2^32 bytes).
+ */
+int lsv_attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k, float descale_v,
+                     void* o, float* lse, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                     int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale, void* stream);
 
 /* Workspace bytes lsv_attn_bwd needs: two fp32 values per (head, token), i.e.
  * 8 * total_tokens * n_heads. Returns -1 for a negative size or n_heads < 1. */

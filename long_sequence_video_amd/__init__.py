@@ -16,13 +16,13 @@ import math
 import os
 
 __all__ = [
-    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size",
+    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_attn_fwd_fp8", "attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size",
     "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak", "lsv_tile_config", "attn_fwd", "attn_bwd",
     "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
-EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue",
+EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue",
                     "lsv_status_string", "lsv_device_peak", "lsv_tile_config")
 
 LSV_OK = 0
@@ -54,6 +54,9 @@ def load_library(path: str = LIB_PATH):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.lsv_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, vp]
     lib.lsv_attn_fwd.restype = ctypes.c_int
+    f = ctypes.c_float
+    lib.lsv_attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i32, i32, i64, i32, i32, f, vp]
+    lib.lsv_attn_fwd_fp8.restype = ctypes.c_int
     lib.lsv_attn_bwd.argtypes = [vp] * 10 + [i32, i32, i64, i32, i32, ctypes.c_float, vp, i64, vp]
     lib.lsv_attn_bwd.restype = ctypes.c_int
     lib.lsv_attn_bwd_workspace_size.argtypes = [i64, i32]
@@ -76,6 +79,14 @@ def lsv_attn_fwd(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, n_se
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().lsv_attn_fwd(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads,
                                        head_dim, scale, stream)
+
+
+def lsv_attn_fwd_fp8(q: int, k: int, v: int, descale_q: float, descale_k: float, descale_v: float, o: int,
+                     lse: int, cu_seqlens: int, n_seqs: int, max_seqlen: int, total_tokens: int, n_heads: int,
+                     head_dim: int, scale: float, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, o, lse, cu_seqlens, n_seqs,
+                                           max_seqlen, total_tokens, n_heads, head_dim, scale, stream)
 
 
 def lsv_attn_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, cu_seqlens: int,
@@ -282,3 +293,53 @@ def attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None = None,
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_attn_bwd")
     return dq, dk, dv
+
+
+def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, cu_seqlens,
+                 max_seqlen: int | None = None, scale: float | None = None, *, out=None, lse=None, stream=None):
+    """FP8 attention forward on torch tensors (one GPU).
+
+    Args:
+      q8, k8, v8: ``[total_tokens, n_heads, 128]`` e4m3 bytes (``torch.uint8`` or
+        ``torch.float8_e4m3fn``), contiguous.
+      descale_q, descale_k, descale_v: per-tensor descales (real value = descale * byte value).
+      cu_seqlens, max_seqlen, scale, out, lse, stream: as for ``attn_fwd``.
+
+    Returns:
+      ``(out, lse)``: bfloat16 ``[T, H, 128]`` and float32 ``[H, T]``.
+    """
+    import torch
+    tensors = (q8, k8, v8)
+    if any(t.element_size() != 1 or t.is_floating_point() and t.dtype != torch.float8_e4m3fn for t in tensors):
+        raise ValueError("q8, k8, v8 must be uint8 or float8_e4m3fn")
+    if q8.dim() != 3 or k8.shape != q8.shape or v8.shape != q8.shape:
+        raise ValueError("q8, k8, v8 must share one [total_tokens, heads, head_dim] shape")
+    if not all(t.is_contiguous() for t in tensors):
+        raise ValueError("q8, k8, v8 must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    dev = q8.device
+    if dev.type != "cuda" or any(t.device != dev for t in (k8, v8, cu_seqlens)):
+        raise ValueError("all tensors must be on the same GPU")
+    total, heads, dim = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    if out is None:
+        out = torch.empty((total, heads, dim), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+    if tuple(out.shape) != (total, heads, dim) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [total_tokens, heads, head_dim] tensor")
+    if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), descale_q, descale_k, descale_v,
+                              out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                              max_seqlen, total, heads, dim, scale, s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_fwd_fp8")
+    return out, lse

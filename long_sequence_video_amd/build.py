@@ -1,6 +1,6 @@
 """Build the native libraries in-tree.
 
-* ``liblsv.so``  — the HIP library (attention forward and backward, QKV prologue; C ABI in
+* ``liblsv.so``  — the HIP library (attention forward, FP8 forward, backward, QKV prologue; C ABI in
   ``include/lsv.h``), gfx950 only.
 * ``inputs/liblsvgen.so`` — the seeded input generator (plain C, OpenMP).
 
@@ -16,7 +16,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-HIP_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "qkv_prologue.hip")]
+HIP_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "qkv_prologue.hip")]
 HIP_LIB = os.path.join(PKG, "liblsv.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"

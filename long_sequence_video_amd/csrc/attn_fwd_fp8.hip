@@ -1,0 +1,403 @@
+// FP8 (e4m3) variant of the dense non-causal varlen attention forward for gfx950 (MI355X).
+//
+// The operation: TensorRT-LLM PR #21275 (the MiniMax-H3 recipe commit: cuDNN attention with
+// --qk-dtype fp8 --v-dtype fp8, per-tensor FP8 descales, the LSE returned) over the varlen
+// forward of FastVideo #2049 (flash_attn_cute.py). Inputs are OCP e4m3 bytes with per-tensor
+// descales dq, dk, dv; for every segment, head and query row i:
+//   z_ij = scale dq dk (q8_i . k8_j),  O_i = dv sum_j softmax_j(z_ij) v8_j,  LSE_i = ln sum_j e^z_ij.
+//
+// Design (gfx950, wave64), following the BF16 kernel:
+//  * One workgroup = 8 waves = 256 query rows, two waves per SIMD; each wave owns 32 queries.
+//  * Key tiles of 64 rows (one v_mfma_f32_32x32x64_f8f6f4 reduces over 64): S^T = K Q^T is four
+//    MFMAs per tile (two 32-key halves x two 64-dim halves), A = K rows from LDS, B = Q^T in
+//    registers; a lane gets one query and 32 of the 64 keys (16 per half).
+//  * P is quantised to e4m3 in place of the score accumulators and is the B operand of
+//    O^T += V^T P^T (four MFMAs, one per 32-dim block): the MFMA pairs byte j of an A lane
+//    with byte j of the B lane of the same half, so P's bytes only need V^T's bytes in the
+//    same key order; V^T is read with ds_read_b64_tr_b8 (a lane gets one column of 8 rows).
+//  * The sum of the quantised weights comes from one more MFMA per tile with an all-ones A:
+//    O is divided by exactly the weights its product used (no fp8 dot instruction on gfx950).
+//    The LSE uses the fp32 sum of the unquantised weights.
+//  * Softmax: p = exp2(s c - m c + 5) with c = scale dq dk log2(e) and m a running row max
+//    raised only when a tile exceeds it by more than 3 log2 units (then O and the sums are
+//    rescaled): weights stay in [0, 2^8], below e4m3's 448 (its conversion does not saturate),
+//    and keys up to ~14 log2 units below the max keep a representable weight. A fixed
+//    first-tile reference, as in the BF16 kernel, would overflow e4m3's range whenever a
+//    later key exceeds the first tile by 3.8 log2 units, which long rows do routinely.
+//  * LDS: K and V rows of 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7),
+//    which keeps 16 consecutive rows (the row reads) and the 8 rows of a transposed read on
+//    distinct banks. K and V stream through an 8-slot ring, 4 tiles ahead, one barrier per tile.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "lsv.h"
+#include "tile_ops.h"
+
+namespace {
+
+using namespace lsv_tiles;
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+constexpr int kD = 128;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBQ = kWaves * 32;          // query rows per workgroup
+constexpr int kBK = 64;                   // keys per tile
+constexpr int kRow8 = kD;                 // bytes per fp8 row
+constexpr int kSlot = kBK * kRow8;        // 8 KB per tile
+constexpr int kSlots = 8;
+constexpr int kAhead = 4;
+constexpr int kRingBytes = kSlots * kSlot;
+constexpr int kLdsBytes = 2 * kRingBytes;
+constexpr int kOpsPerTile = 2;            // one 1 KB copy of K and one of V per wave per tile
+constexpr float kRefLog2 = 5.0f;          // the reference weight: 2^5
+constexpr float kLazyLog2 = 3.0f;         // raise the running max only beyond this (log2 units)
+constexpr unsigned kOnes = 0x38383838u;   // four e4m3 ones
+static_assert(kAhead >= 2 && kAhead <= kSlots - 2, "ring too small for the prefetch distance");
+
+__device__ __forceinline__ int sw8(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Key of byte j (0..31) of a P^T / V^T operand in lane half h: byte j = 16 a + v holds
+// accumulator element v of key half a, i.e. key 32 a + 8 (v / 4) + 4 h + v % 4.
+__device__ __forceinline__ int key_of(int h, int j) {
+  return 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h + (j & 3);
+}
+
+struct Lane {
+  int lane, h32, l32;
+  unsigned kaddr[8];   // K row reads (slot 0): index 4 a + 2 c2 + sub
+  unsigned vaddr[16];  // V^T transposed reads (slot 0, V ring): index 4 db + r
+};
+
+struct Ctx {
+  unsigned lds_copy;   // this wave's 1 KB block of ring slot 0 (uniform)
+  const char* kbase;   // k row seg_start, this head (uniform)
+  const char* vbase;
+  unsigned row_stride;
+  int crow;            // the tile row this lane copies
+  unsigned coff;       // the byte offset of its chunk inside the row
+  unsigned cconst;     // crow * row_stride + coff
+  int seg_len;
+  float c;             // scale dq dk log2(e)
+};
+
+struct Acc {
+  f32x16 O[4];   // O^T, d-block db
+  f32x16 LB;     // every element: sum of the quantised weights (for this lane's query)
+  float m;       // reference (raw score units)
+  float l;       // fp32 sum of the weights, for the LSE
+};
+
+// Tile t (segments of 64 keys or more): rows min(64 t, seg_len - 64) .. +63; wave w copies
+// rows 8w .. 8w+7, lane i the 16 bytes of LDS chunk position i % 8 of row 8w + i / 8.
+__device__ __forceinline__ void load_tile(const Ctx& cx, int t) {
+  const unsigned slot = (unsigned)(t & (kSlots - 1)) * kSlot;
+  const unsigned off = (unsigned)min(t * kBK, cx.seg_len - kBK) * cx.row_stride;
+  dma16(cx.cconst, cx.kbase + off, cx.lds_copy + slot);
+  dma16(cx.cconst, cx.vbase + off, cx.lds_copy + slot + kRingBytes);
+}
+// A single tile shorter than 64 keys: rows past the segment repeat its last row.
+__device__ __forceinline__ void load_tile_short(const Ctx& cx, int t) {
+  const unsigned slot = (unsigned)(t & (kSlots - 1)) * kSlot;
+  const unsigned r = (unsigned)min(cx.crow, cx.seg_len - 1);
+  dma16(__umul24(r, cx.row_stride) + cx.coff, cx.kbase, cx.lds_copy + slot);
+  dma16(__umul24(r, cx.row_stride) + cx.coff, cx.vbase, cx.lds_copy + slot + kRingBytes);
+}
+
+__device__ __forceinline__ i32x8 k_operand(const Lane& ln, unsigned slot, int a, int c2) {
+  const u32x4 x = *(lds_u32x4*)(uintptr_t)(ln.kaddr[4 * a + 2 * c2] + slot);
+  const u32x4 y = *(lds_u32x4*)(uintptr_t)(ln.kaddr[4 * a + 2 * c2 + 1] + slot);
+  i32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (int)x[i];
+    r[4 + i] = (int)y[i];
+  }
+  return r;
+}
+
+__device__ __forceinline__ i32x8 v_operand(const Lane& ln, unsigned slot, int db) {
+  i32x8 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(ln.vaddr[4 * db + q] + slot));
+    r[2 * q] = x[0];
+    r[2 * q + 1] = x[1];
+  }
+  return r;
+}
+
+// S^T for the two key halves of the tile in `slot`.
+__device__ __forceinline__ void qk_tile(unsigned slot, const i32x8 (&qr)[2], const Lane& ln, f32x16 (&S)[2]) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    f32x16 s = {};
+    s = mfma8(k_operand(ln, slot, a, 0), qr[0], s);
+    s = mfma8(k_operand(ln, slot, a, 1), qr[1], s);
+    S[a] = s;
+  }
+}
+
+// Keys of the tile before `skip` (shifted last tile) or from `valid` on (short tile) get -inf.
+__device__ __forceinline__ void mask_head(f32x16 (&S)[2], int skip, int h32) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (32 * a + 8 * (v >> 2) + 4 * h32 + (v & 3) < skip) S[a][v] = -INFINITY;
+}
+__device__ __forceinline__ void mask_tail(f32x16 (&S)[2], int valid, int h32) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (32 * a + 8 * (v >> 2) + 4 * h32 + (v & 3) >= valid) S[a][v] = -INFINITY;
+}
+
+__device__ __forceinline__ float lane_max(const f32x16 (&S)[2]) {
+  float m = fmaxf(S[0][0], S[1][0]);
+#pragma unroll
+  for (int v = 1; v < 16; ++v) m = fmaxf(m, fmaxf(S[0][v], S[1][v]));
+  return m;
+}
+
+// Weights of 4 consecutive bytes (dword w of the P operand): exp2(s c - R), summed into l,
+// quantised to e4m3.
+__device__ __forceinline__ void softmax_dword(const f32x16 (&S)[2], i32x8& P, float& l, float c, float nr, int w) {
+  const int a = w >> 2, v0 = 4 * (w & 3);
+  float e[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    e[b] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a][v0 + b], c, nr));
+    l += e[b];
+  }
+  unsigned d = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0u, false);
+  d = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], d, true);
+  P[w] = (int)d;
+}
+
+__device__ __forceinline__ void pv_tile(Acc& acc, unsigned slot, const i32x8& P, const Lane& ln, const i32x8& ones) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc.O[db] = mfma8(v_operand(ln, slot, db), P, acc.O[db]);
+  acc.LB = mfma8(ones, P, acc.LB);
+}
+
+// The key loop: online softmax with a lazily raised row max. Each tile's scores are compared
+// with the current max m; only when some row of the wave exceeds it by more than 3 log2 units
+// (wave-uniform, rare after the first tiles) is m raised and O and the sums rescaled. Weights
+// exp2(s c - m c + 5) then never exceed 2^8 < 448, so their e4m3 rounding cannot overflow.
+__device__ __forceinline__ void run_online(const Ctx& cx, int n_kt, Acc& acc, const i32x8 (&qr)[2], const Lane& ln,
+                                           const i32x8& ones) {
+  if (n_kt >= 2) {
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) load_tile(cx, t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) load_tile_short(cx, t);
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc.O[db] = f32x16{};
+  acc.LB = f32x16{};
+  acc.l = 0.f;
+  acc.m = -INFINITY;
+  const float lazy = kLazyLog2 / cx.c;
+  f32x16 S[2];
+  i32x8 P;
+  for (int t = 0; t < n_kt; ++t) {
+    const unsigned slot = (unsigned)(t & (kSlots - 1)) * kSlot;
+    wait_vmcnt<kOpsPerTile * (kAhead - 1)>();
+    barrier_lds();
+    if (n_kt >= 2) load_tile(cx, t + kAhead);
+    qk_tile(slot, qr, ln, S);
+    if (t == n_kt - 1) {
+      if (n_kt >= 2) mask_head(S, kBK * n_kt - cx.seg_len, ln.h32);
+      else mask_tail(S, cx.seg_len, ln.h32);
+    }
+    const float mx = pair_max(lane_max(S));
+    if (__builtin_amdgcn_ballot_w64(mx > acc.m + lazy) != 0) {  // wave-uniform
+      const float mnew = fmaxf(acc.m, mx);
+      const float r = __builtin_amdgcn_exp2f((acc.m - mnew) * cx.c);  // 0 on the first tile
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc.O[db][v] *= r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.LB[v] *= r;
+      acc.l *= r;
+      acc.m = mnew;
+    }
+    const float nr = kRefLog2 - acc.m * cx.c;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) softmax_dword(S, P, acc.l, cx.c, nr, w);
+    pv_tile(acc, slot, P, ln, ones);
+  }
+  wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS past this point
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                    uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                    int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
+                    float dv, int n_logical) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
+  const int per_xcd = gridDim.x >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= n_logical) return;
+  const int qt = logical % tiles_per_seq;
+  const int hs = logical / tiles_per_seq;
+  const int seg = hs % n_seqs;
+  const int head = hs / n_seqs;
+  const int seg_start = cu_seqlens[seg];
+  const int seg_end = cu_seqlens[seg + 1];
+  if (seg_start < 0 || seg_end < seg_start || (int64_t)seg_end > total_tokens) return;
+  const int seg_len = seg_end - seg_start;
+  if (seg_len > max_seqlen) return;
+  const int q0 = qt * kBQ;
+  if (q0 >= seg_len) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const unsigned lds_base = (unsigned)(uintptr_t)(lds_char*)smem_generic;
+  Ctx cx;
+  cx.lds_copy = lds_base + wave * 1024;
+  cx.row_stride = (unsigned)n_heads * kRow8;
+  cx.kbase = (const char*)k + ((int64_t)seg_start * n_heads + head) * kRow8;
+  cx.vbase = (const char*)v + ((int64_t)seg_start * n_heads + head) * kRow8;
+  {
+    const int i = tid & 63;
+    cx.crow = 8 * wave + (i >> 3);
+    cx.coff = (unsigned)(((i & 7) ^ sw8(cx.crow)) * 16);
+    cx.cconst = (unsigned)cx.crow * cx.row_stride + cx.coff;
+  }
+  cx.seg_len = seg_len;
+  cx.c = c;
+  const int n_kt = (seg_len + kBK - 1) / kBK;
+
+  Lane ln;
+  ln.lane = tid & 63;
+  ln.h32 = ln.lane >> 5;
+  ln.l32 = ln.lane & 31;
+  // K rows: lane (key l32 of half a, h32) reads dims 64 c2 + 32 h32 .. +31, i.e. chunks
+  // 4 c2 + 2 h32 + sub of row 32 a + l32.
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int row = 32 * a + ln.l32;
+        const int chunk = 4 * c2 + 2 * ln.h32 + sub;
+        ln.kaddr[4 * a + 2 * c2 + sub] = lds_base + row * kRow8 + ((chunk ^ sw8(row)) << 4);
+      }
+  // V^T (d-block db, read r): in 16-lane group (m0, h32) lane L gives the address of row
+  // key_of(h32, 8 r + L / 2), columns 32 db + m0 + 8 (L % 2) .. +7; the read returns to lane L
+  // column 32 db + m0 + L of those 8 rows.
+  {
+    const int L = ln.lane & 15, m0 = 16 * ((ln.lane >> 4) & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = key_of(ln.h32, 8 * r + (L >> 1));
+        const int col = 32 * db + m0 + 8 * (L & 1);
+        ln.vaddr[4 * db + r] = lds_base + kRingBytes + row * kRow8 + (((col >> 4) ^ sw8(row)) << 4) + (col & 15);
+      }
+  }
+
+  // Q^T operand: lane (query l32, h32) holds dims 64 c2 + 32 h32 .. +31 for c2 = 0, 1.
+  i32x8 qr[2];
+  {
+    int row = q0 + wave * 32 + ln.l32;
+    row = row < seg_len ? row : seg_len - 1;
+    const uint8_t* qrow = q + ((int64_t)(seg_start + row) * n_heads + head) * kRow8 + 32 * ln.h32;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const u32x4 x = *(const u32x4*)(qrow + 64 * c2);
+      const u32x4 y = *(const u32x4*)(qrow + 64 * c2 + 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qr[c2][i] = (int)x[i];
+        qr[c2][4 + i] = (int)y[i];
+      }
+    }
+  }
+  i32x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (int)kOnes;
+
+  Acc acc;
+  run_online(cx, n_kt, acc, qr, ln, ones);
+
+  // O = dv (P V) / sum(P) -> bf16; LSE = (m c - 5 + log2 l) ln 2.
+  const float l = pair_sum(acc.l);
+  const float lb = acc.LB[0];
+  const float mul = dv / lb;
+  const int row = q0 + wave * 32 + ln.l32;
+  if (row < seg_len) {
+    const int64_t tok = (int64_t)seg_start + row;
+    uint16_t* orow = o + (tok * n_heads + head) * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x2 lo, hi;
+        lo[0] = (__bf16)(acc.O[db][4 * g + 0] * mul);
+        lo[1] = (__bf16)(acc.O[db][4 * g + 1] * mul);
+        hi[0] = (__bf16)(acc.O[db][4 * g + 2] * mul);
+        hi[1] = (__bf16)(acc.O[db][4 * g + 3] * mul);
+        u32x2 pk;
+        pk[0] = __builtin_bit_cast(unsigned, lo);
+        pk[1] = __builtin_bit_cast(unsigned, hi);
+        *(u32x2*)(orow + 32 * db + 8 * g + 4 * ln.h32) = pk;
+      }
+    if (ln.h32 == 0) lse[(int64_t)head * total_tokens + tok] = (acc.m * c - kRefLog2 + __log2f(l)) * 0.69314718055994530942f;
+  }
+}
+
+}  // namespace
+
+extern "C" int lsv_attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                                float descale_v, void* o, float* lse, const int32_t* cu_seqlens, int32_t n_seqs,
+                                int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                                float scale, void* stream) {
+  if (n_seqs < 0 || max_seqlen < 0 || total_tokens < 0 || n_heads < 1) return LSV_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return LSV_ERR_INVALID_ARG;
+  if (!(descale_q > 0.f) || !(descale_k > 0.f) || !(descale_v > 0.f) || !isfinite(descale_q) ||
+      !isfinite(descale_k) || !isfinite(descale_v))
+    return LSV_ERR_INVALID_ARG;
+  if (head_dim != kD) return LSV_ERR_UNSUPPORTED;
+  if (n_seqs == 0 || max_seqlen == 0 || total_tokens == 0) return LSV_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return LSV_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return LSV_ERR_ALIGNMENT;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return LSV_ERR_ALIGNMENT;
+  if (total_tokens > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  const int64_t row_stride = (int64_t)n_heads * kRow8;
+  if (row_stride >= (1 << 24) || (int64_t)max_seqlen >= (1 << 24) ||
+      (int64_t)max_seqlen * row_stride + kRow8 > (int64_t)UINT32_MAX)
+    return LSV_ERR_UNSUPPORTED;
+  const int64_t tiles = ((int64_t)max_seqlen + kBQ - 1) / kBQ;
+  const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
+  const int64_t grid = (n_logical + 7) / 8 * 8;
+  if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  const float c = (float)((double)scale * (double)descale_q * (double)descale_k * 1.4426950408889634074);
+  if (!(c > 0.f) || !isfinite(c)) return LSV_ERR_INVALID_ARG;
+  if (hipFuncSetAttribute((const void*)attn_fwd_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return LSV_ERR_HIP;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attn_fwd_fp8_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
+                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, cu_seqlens,
+                     (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, descale_v,
+                     (int)n_logical);
+  if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
+  return LSV_OK;
+}

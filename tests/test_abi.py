@@ -153,3 +153,29 @@ def test_bwd_validation_before_any_hip_call(args, code):
                           a["n_seqs"], a["max_seqlen"], a["total_tokens"], a["n_heads"], a["head_dim"], a["scale"],
                           a["ws"], a["ws_bytes"], None)
     assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dq=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dk=-1.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dv=float("inf")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dq=float("nan")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dq=1e30, dk=1e30), lsv.LSV_ERR_INVALID_ARG),     # scale * dq * dk overflows fp32
+    (dict(q=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(k=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(lse=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(max_seqlen=599_187, total_tokens=599_187, n_heads=56), lsv.LSV_ERR_UNSUPPORTED),  # 32-bit offsets
+    (dict(n_seqs=0), lsv.LSV_OK),
+    (dict(total_tokens=0), lsv.LSV_OK),
+])
+def test_fp8_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, dq=0.01, dk=0.01, dv=0.01, n_seqs=1, max_seqlen=10, total_tokens=10,
+             n_heads=4, head_dim=128, scale=0.125)
+    a.update(args)
+    rc = lsv.lsv_attn_fwd_fp8(a["q"], a["k"], a["v"], a["dq"], a["dk"], a["dv"], a["o"], a["lse"], a["cu"],
+                              a["n_seqs"], a["max_seqlen"], a["total_tokens"], a["n_heads"], a["head_dim"],
+                              a["scale"], None)
+    assert rc == code
