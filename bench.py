@@ -6,8 +6,11 @@ clips, 19,394 + 38,000 + 104,000 tokens x 56 heads x 128 (161,394 tokens; 3.623e
 per step). Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
-                  [--no-prologue] [--prologue-only] [--no-bwd] [--bwd-only]
+                  [--no-prologue] [--prologue-only] [--no-bwd] [--bwd-only] [--no-fp8] [--fp8-only]
   python bench.py --copy-bytes N   # a plain device copy of N bytes, to calibrate HBM counters
+
+An object ``attn_fwd_fp8`` times the FP8 (e4m3) forward on the same pack quantised per tensor,
+with the same flop count, against MI355X's dense FP8 peak (5.0 PFLOP/s).
 
 An object ``attn_bwd`` times the backward (dQ, dK, dV; deterministic, three kernels) on the
 same pack, counted the usual way as 2.5 x the forward's flops (the five products of the
@@ -136,6 +139,49 @@ def bench_prologue(steps: int, warmup: int):
     }
 
 
+PEAK_FP8_TFLOPS = 5000.0  # MI355X published dense FP8 MFMA peak (5.0 PFLOP/s)
+
+
+def bench_fp8(name: str, steps: int, warmup: int):
+    """Time the FP8 forward on workload ``name`` quantised per tensor; returns the JSON object."""
+    import torch
+    import long_sequence_video_amd as lsv
+    from long_sequence_video_amd import inputs as gen
+    dev = torch.device("cuda:0")
+    f8 = gen.quantize_fp8(make_inputs(name))
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (f8.q, f8.k, f8.v))
+    cu = torch.from_numpy(f8.cu_seqlens).to(dev)
+    out = torch.empty(f8.q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((f8.n_heads, f8.total_tokens), dtype=torch.float32, device=dev)
+
+    def step():
+        lsv.attn_fwd_fp8(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale, out=out,
+                         lse=lse)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    tf = f8.flops() / (ms * 1e-3) / 1e12
+    log(f"{name} fp8: {ms:.3f} ms, {tf:.1f} TFLOP/s, {100 * tf / PEAK_FP8_TFLOPS:.1f}% of the FP8 peak")
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return {
+        "workload": name + " (e4m3, per-tensor descales)", "ms_per_step": round(ms, 4), "steps": steps,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "kernel": "attn_fwd_fp8_kernel",
+                     # plus the weight-sum MFMA: half of a 32x32x64 per eight
+                     "mfma_flops_executed": f8.flops() * (17.0 / 16.0)},
+    }
+
+
 def bench_backward(name: str, steps: int, warmup: int):
     """Time the attention backward on workload ``name``; returns the JSON object."""
     import torch
@@ -255,6 +301,8 @@ def main():
     ap.add_argument("--no-prologue", action="store_true", help="skip the QKV-prologue leg")
     ap.add_argument("--prologue-only", action="store_true", help="time only the QKV prologue (for profiling)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward leg")
+    ap.add_argument("--fp8-only", action="store_true", help="time only the FP8 forward (for profiling)")
     ap.add_argument("--bwd-only", action="store_true", help="time only the backward (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -276,6 +324,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.prologue_only:
         print(json.dumps({"qkv_prologue": bench_prologue(args.steps, args.warmup)}), flush=True)
+        return
+    if args.fp8_only:
+        print(json.dumps({"attn_fwd_fp8": bench_fp8(args.config, args.steps, args.warmup)}), flush=True)
         return
     if args.bwd_only:
         print(json.dumps({"attn_bwd": bench_backward(args.config, args.steps, args.warmup)}), flush=True)
@@ -356,6 +407,8 @@ def main():
     }
     del q, k, v, out, lse
     torch.cuda.empty_cache()
+    if not args.no_fp8:
+        result["attn_fwd_fp8"] = bench_fp8(args.config, min(max(args.steps, 3), 10), max(min(args.warmup, 2), 1))
     if not args.no_bwd:
         result["attn_bwd"] = bench_backward(args.config, min(max(args.steps, 3), 5), max(min(args.warmup, 2), 1))
     if not args.no_prologue:

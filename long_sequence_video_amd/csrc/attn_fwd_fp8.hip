@@ -15,13 +15,18 @@
 //    O^T += V^T P^T (four MFMAs, one per 32-dim block): the MFMA pairs byte j of an A lane
 //    with byte j of the B lane of the same half, so P's bytes only need V^T's bytes in the
 //    same key order; V^T is read with ds_read_b64_tr_b8 (a lane gets one column of 8 rows).
-//  * The sum of the quantised weights comes from one more MFMA per tile with an all-ones A:
-//    O is divided by exactly the weights its product used (no fp8 dot instruction on gfx950).
-//    The LSE uses the fp32 sum of the unquantised weights.
+//  * The sum of the quantised weights comes from one more, half-size MFMA per tile
+//    (v_mfma_f32_16x16x128_f8f6f4 with a 0/1 selection A that routes each query's 64 bytes
+//    of P into one output element): O is divided by exactly the weights its product used
+//    (no fp8 dot instruction on gfx950). The LSE uses the fp32 sum of the unquantised weights.
+//  * Software pipeline per key tile t: one sequence of nine MFMAs, S(t+1) = Q K(t+1)^T, then
+//    O += P(t-1) V(t-1) and the weight sum of P(t-1), with the exp2 / e4m3 work of S(t) placed
+//    between them (scheduling barriers hold the order).
 //  * Softmax: p = exp2(s c - m c + 5) with c = scale dq dk log2(e) and m a running row max
 //    raised only when a tile exceeds it by more than 3 log2 units (then O and the sums are
-//    rescaled): weights stay in [0, 2^8], below e4m3's 448 (its conversion does not saturate),
-//    and keys up to ~14 log2 units below the max keep a representable weight. A fixed
+//    rescaled, O after the tile's MFMAs): weights stay in [0, 2^8], below e4m3's 448 (its
+//    conversion does not saturate), and keys up to ~14 log2 units below the max keep a
+//    representable weight. A fixed
 //    first-tile reference, as in the BF16 kernel, would overflow e4m3's range whenever a
 //    later key exceeds the first tile by 3.8 log2 units, which long rows do routinely.
 //  * LDS: K and V rows of 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7),
@@ -74,8 +79,8 @@ __device__ __forceinline__ int key_of(int h, int j) {
 
 struct Lane {
   int lane, h32, l32;
-  unsigned kaddr[8];   // K row reads (slot 0): index 4 a + 2 c2 + sub
-  unsigned vaddr[16];  // V^T transposed reads (slot 0, V ring): index 4 db + r
+  unsigned kaddr[4];   // K row reads, ring slot 0, key half 0: index 2 c2 + sub (key half a: + 4096 a)
+  unsigned vaddr[4];   // V^T transposed reads, V ring slot 0, read 0: index db (read r: + 2048 r)
 };
 
 struct Ctx {
@@ -88,12 +93,13 @@ struct Ctx {
   unsigned cconst;     // crow * row_stride + coff
   int seg_len;
   float c;             // scale dq dk log2(e)
+  float lazy;          // kLazyLog2 / c: the max margin in raw score units
 };
 
 struct Acc {
   f32x16 O[4];   // O^T, d-block db
-  f32x16 LB;     // every element: sum of the quantised weights (for this lane's query)
-  float m;       // reference (raw score units)
+  f32x4 LB;      // element 0 of lanes 0..31: sum of the quantised weights of query l32 (else 0)
+  float m;       // running row max (raw score units)
   float l;       // fp32 sum of the weights, for the LSE
 };
 
@@ -113,9 +119,24 @@ __device__ __forceinline__ void load_tile_short(const Ctx& cx, int t) {
   dma16(__umul24(r, cx.row_stride) + cx.coff, cx.vbase, cx.lds_copy + slot + kRingBytes);
 }
 
-__device__ __forceinline__ i32x8 k_operand(const Lane& ln, unsigned slot, int a, int c2) {
-  const u32x4 x = *(lds_u32x4*)(uintptr_t)(ln.kaddr[4 * a + 2 * c2] + slot);
-  const u32x4 y = *(lds_u32x4*)(uintptr_t)(ln.kaddr[4 * a + 2 * c2 + 1] + slot);
+// Lane read bases of one ring slot (one add each; the rest of every read address is an
+// immediate offset).
+struct Bases {
+  unsigned k[4], v[4];
+};
+__device__ __forceinline__ Bases bases(const Lane& ln, unsigned kslot, unsigned vslot) {
+  Bases b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b.k[i] = ln.kaddr[i] + kslot;
+    b.v[i] = ln.vaddr[i] + vslot;
+  }
+  return b;
+}
+
+__device__ __forceinline__ i32x8 k_operand(const Bases& b, int a, int c2) {
+  const u32x4 x = *(lds_u32x4*)(uintptr_t)(b.k[2 * c2] + 4096u * a);
+  const u32x4 y = *(lds_u32x4*)(uintptr_t)(b.k[2 * c2 + 1] + 4096u * a);
   i32x8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -125,24 +146,24 @@ __device__ __forceinline__ i32x8 k_operand(const Lane& ln, unsigned slot, int a,
   return r;
 }
 
-__device__ __forceinline__ i32x8 v_operand(const Lane& ln, unsigned slot, int db) {
+__device__ __forceinline__ i32x8 v_operand(const Bases& b, int db) {
   i32x8 r;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(ln.vaddr[4 * db + q] + slot));
+    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(b.v[db] + 2048u * q));
     r[2 * q] = x[0];
     r[2 * q + 1] = x[1];
   }
   return r;
 }
 
-// S^T for the two key halves of the tile in `slot`.
-__device__ __forceinline__ void qk_tile(unsigned slot, const i32x8 (&qr)[2], const Lane& ln, f32x16 (&S)[2]) {
+// S^T for the two key halves of a tile.
+__device__ __forceinline__ void qk_tile(const Bases& b, const i32x8 (&qr)[2], f32x16 (&S)[2]) {
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     f32x16 s = {};
-    s = mfma8(k_operand(ln, slot, a, 0), qr[0], s);
-    s = mfma8(k_operand(ln, slot, a, 1), qr[1], s);
+    s = mfma8(k_operand(b, a, 0), qr[0], s);
+    s = mfma8(k_operand(b, a, 1), qr[1], s);
     S[a] = s;
   }
 }
@@ -163,15 +184,17 @@ __device__ __forceinline__ void mask_tail(f32x16 (&S)[2], int valid, int h32) {
       if (32 * a + 8 * (v >> 2) + 4 * h32 + (v & 3) >= valid) S[a][v] = -INFINITY;
 }
 
-__device__ __forceinline__ float lane_max(const f32x16 (&S)[2]) {
+// Max over the row (this lane's 32 scores and its partner's).
+__device__ __forceinline__ float row_max(const f32x16 (&S)[2]) {
   float m = fmaxf(S[0][0], S[1][0]);
 #pragma unroll
-  for (int v = 1; v < 16; ++v) m = fmaxf(m, fmaxf(S[0][v], S[1][v]));
-  return m;
+  for (int v = 1; v < 16; ++v) m = fmaxf(fmaxf(m, S[0][v]), S[1][v]);
+  return pair_max(m);
 }
 
-// Weights of 4 consecutive bytes (dword w of the P operand): exp2(s c - R), summed into l,
-// quantised to e4m3.
+// Weights of 4 consecutive bytes (dword w of the P operand): exp2(s c + nr), summed into l,
+// quantised to e4m3. The upper half of P[w] is written by the second conversion, so the
+// first one may keep whatever P[w] held.
 __device__ __forceinline__ void softmax_dword(const f32x16 (&S)[2], i32x8& P, float& l, float c, float nr, int w) {
   const int a = w >> 2, v0 = 4 * (w & 3);
   float e[4];
@@ -180,23 +203,121 @@ __device__ __forceinline__ void softmax_dword(const f32x16 (&S)[2], i32x8& P, fl
     e[b] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a][v0 + b], c, nr));
     l += e[b];
   }
-  unsigned d = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0u, false);
+  unsigned d = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], (unsigned)P[w], false);
   d = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], d, true);
   P[w] = (int)d;
 }
-
-__device__ __forceinline__ void pv_tile(Acc& acc, unsigned slot, const i32x8& P, const Lane& ln, const i32x8& ones) {
+__device__ __forceinline__ void softmax_all(const f32x16 (&S)[2], i32x8& P, float& l, float c, float nr) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc.O[db] = mfma8(v_operand(ln, slot, db), P, acc.O[db]);
-  acc.LB = mfma8(ones, P, acc.LB);
+  for (int w = 0; w < 8; ++w) softmax_dword(S, P, l, c, nr, w);
 }
 
-// The key loop: online softmax with a lazily raised row max. Each tile's scores are compared
-// with the current max m; only when some row of the wave exceeds it by more than 3 log2 units
-// (wave-uniform, rare after the first tiles) is m raised and O and the sums rescaled. Weights
-// exp2(s c - m c + 5) then never exceed 2^8 < 448, so their e4m3 rounding cannot overflow.
-__device__ __forceinline__ void run_online(const Ctx& cx, int n_kt, Acc& acc, const i32x8 (&qr)[2], const Lane& ln,
-                                           const i32x8& ones) {
+// The weight sums: one 16x16x128 MFMA whose A selects, for output row 0, the lanes of
+// queries 0..15 (lane blocks 0 and 2 of B) and, for row 4, those of queries 16..31 (blocks 1
+// and 3); row 0 lands in element 0 of lanes 0..15 and row 4 in element 0 of lanes 16..31,
+// i.e. each sum in the lane whose l32 is its query.
+__device__ __forceinline__ f32x4 mfma_sum(const i32x8& sel, const i32x8& P, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, P, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void pv_tile(Acc& acc, const Bases& b, const i32x8& P, const i32x8& sel) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc.O[db] = mfma8(v_operand(b, db), P, acc.O[db]);
+  acc.LB = mfma_sum(sel, P, acc.LB);
+}
+
+// Raising the running max from m to mnew rescales everything summed against m by
+// r = exp2((m - mnew) c).
+__device__ __forceinline__ void scale_o(Acc& acc, float r) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc.O[db][v] *= r;
+  acc.LB[0] *= r;
+}
+
+__device__ __forceinline__ unsigned slot_of(int t) { return (unsigned)(t & (kSlots - 1)) * kSlot; }
+
+// Steady-state key tile t (1 <= t <= n_kt - 2). On entry S(t) and P(t-1) are complete and
+// tile t+1 is in LDS. First the lazy max check of S(t): if some row of the wave exceeds its
+// max by more than the margin (rare), the max is raised and l rescaled at once, and O and
+// the weight sums after this tile's MFMAs (which still add P(t-1) V(t-1), weighted against
+// the old max). Then one sequence of nine MFMAs, S(t+1) = Q K(t+1)^T (four, first, so that
+// the next tile's max check finds them done), O += P(t-1) V(t-1) (four), the weight sum of
+// P(t-1), with the weights P(t) of S(t) computed between them, operands read one MFMA
+// ahead and the copy of tile t + kAhead issued after the fifth.
+// Then tile t+2 is waited for and the workgroup synchronises.
+__device__ __forceinline__ void step(const Ctx& cx, int t, Acc& acc, const f32x16 (&Scur)[2], f32x16 (&Snext)[2],
+                                     const i32x8& Pprev, i32x8& Pcur, const i32x8 (&qr)[2], const Lane& ln,
+                                     const i32x8& sel) {
+  const float mx = row_max(Scur);
+  const bool raise = __builtin_amdgcn_ballot_w64(mx > acc.m + cx.lazy) != 0;  // wave-uniform
+  float r = 1.f;
+  if (raise) {
+    const float mnew = fmaxf(acc.m, mx);
+    r = __builtin_amdgcn_exp2f((acc.m - mnew) * cx.c);
+    acc.l *= r;
+    acc.m = mnew;
+  }
+  const float nr = kRefLog2 - acc.m * cx.c;
+  const Bases b = bases(ln, slot_of(t + 1), slot_of(t - 1));
+  i32x8 opnd[9];
+  auto read = [&](int n) {
+    if (n < 4) opnd[n] = k_operand(b, n >> 1, n & 1);
+    else if (n < 8) opnd[n] = v_operand(b, n - 4);
+  };
+  read(0);
+  sched_fence();
+  f32x16 s = {};
+#pragma unroll
+  for (int n = 0; n < 9; ++n) {
+    if (n < 4) {
+      const int a = n >> 1, c2 = n & 1;
+      s = mfma8(opnd[n], qr[c2], c2 ? s : f32x16{});
+      if (c2) Snext[a] = s;
+    } else if (n < 8) {
+      acc.O[n - 4] = mfma8(opnd[n], Pprev, acc.O[n - 4]);
+    } else {
+      acc.LB = mfma_sum(sel, Pprev, acc.LB);
+    }
+    if (n + 1 < 9) read(n + 1);
+    if (n == 4) load_tile(cx, t + kAhead);
+    if (n < 8) softmax_dword(Scur, Pcur, acc.l, cx.c, nr, n);
+    sched_fence();
+  }
+  // P(t) and the sum must be complete here (they must not sink into the next tile).
+  asm volatile("" : "+v"(Pcur), "+v"(acc.l));
+  if (raise) scale_o(acc, r);
+  wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
+  barrier_lds();
+}
+
+// The last tile tl = n_kt - 1 >= 1 (loaded shifted to end at the segment end): P(tl-1) V(tl-1),
+// the masked scores S(tl), the max check, P(tl) V(tl).
+__device__ __forceinline__ void last_tile(const Ctx& cx, int n_kt, Acc& acc, f32x16 (&Slast)[2], const i32x8& Pprev,
+                                          i32x8& Pcur, const Lane& ln, const i32x8& sel) {
+  const int tl = n_kt - 1;
+  pv_tile(acc, bases(ln, 0, slot_of(tl - 1)), Pprev, sel);
+  mask_head(Slast, kBK * n_kt - cx.seg_len, ln.h32);
+  const float mx = row_max(Slast);
+  if (__builtin_amdgcn_ballot_w64(mx > acc.m + cx.lazy) != 0) {
+    const float mnew = fmaxf(acc.m, mx);
+    const float r = __builtin_amdgcn_exp2f((acc.m - mnew) * cx.c);
+    acc.l *= r;
+    acc.m = mnew;
+    scale_o(acc, r);
+  }
+  softmax_all(Slast, Pcur, acc.l, cx.c, kRefLog2 - acc.m * cx.c);
+  pv_tile(acc, bases(ln, 0, slot_of(tl)), Pcur, sel);
+}
+
+// The key loop: online softmax with a lazily raised row max. The first tile sets the max;
+// later a tile raises it (and O and the sums are rescaled) only when some row of the wave
+// exceeds it by more than 3 log2 units, which is wave-uniform and rare after the first tiles.
+// Weights exp2(s c - m c + 5) then never exceed 2^8 < 448, so their e4m3 rounding cannot
+// overflow. S(t) and P(t) alternate between the A and B registers (A for even t).
+__device__ __forceinline__ void run(const Ctx& cx, int n_kt, Acc& acc, const i32x8 (&qr)[2], const Lane& ln,
+                                    const i32x8& sel) {
   if (n_kt >= 2) {
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) load_tile(cx, t);
@@ -206,40 +327,37 @@ __device__ __forceinline__ void run_online(const Ctx& cx, int n_kt, Acc& acc, co
   }
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc.O[db] = f32x16{};
-  acc.LB = f32x16{};
+  acc.LB = f32x4{};
   acc.l = 0.f;
-  acc.m = -INFINITY;
-  const float lazy = kLazyLog2 / cx.c;
-  f32x16 S[2];
-  i32x8 P;
-  for (int t = 0; t < n_kt; ++t) {
-    const unsigned slot = (unsigned)(t & (kSlots - 1)) * kSlot;
-    wait_vmcnt<kOpsPerTile * (kAhead - 1)>();
-    barrier_lds();
-    if (n_kt >= 2) load_tile(cx, t + kAhead);
-    qk_tile(slot, qr, ln, S);
-    if (t == n_kt - 1) {
-      if (n_kt >= 2) mask_head(S, kBK * n_kt - cx.seg_len, ln.h32);
-      else mask_tail(S, cx.seg_len, ln.h32);
-    }
-    const float mx = pair_max(lane_max(S));
-    if (__builtin_amdgcn_ballot_w64(mx > acc.m + lazy) != 0) {  // wave-uniform
-      const float mnew = fmaxf(acc.m, mx);
-      const float r = __builtin_amdgcn_exp2f((acc.m - mnew) * cx.c);  // 0 on the first tile
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc.O[db][v] *= r;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc.LB[v] *= r;
-      acc.l *= r;
-      acc.m = mnew;
-    }
-    const float nr = kRefLog2 - acc.m * cx.c;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) softmax_dword(S, P, acc.l, cx.c, nr, w);
-    pv_tile(acc, slot, P, ln, ones);
+  wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
+  barrier_lds();
+  f32x16 SA[2], SB[2];
+  i32x8 PA = {}, PB = {};
+  qk_tile(bases(ln, 0, 0), qr, SA);
+  if (n_kt == 1) {
+    mask_tail(SA, cx.seg_len, ln.h32);
+    acc.m = row_max(SA);
+    softmax_all(SA, PA, acc.l, cx.c, kRefLog2 - acc.m * cx.c);
+    pv_tile(acc, bases(ln, 0, 0), PA, sel);
+    wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS past this point
+    return;
   }
+  acc.m = row_max(SA);
+  softmax_all(SA, PA, acc.l, cx.c, kRefLog2 - acc.m * cx.c);
+  qk_tile(bases(ln, slot_of(1), 0), qr, SB);
+  load_tile(cx, kAhead);
+  wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
+  barrier_lds();
+
+  const int last = n_kt - 2;
+  int t = 1;
+  for (; t + 1 <= last; t += 2) {
+    step(cx, t, acc, SB, SA, PA, PB, qr, ln, sel);
+    step(cx, t + 1, acc, SA, SB, PB, PA, qr, ln, sel);
+  }
+  if (t <= last) step(cx, t, acc, SB, SA, PA, PB, qr, ln, sel);
+  if ((n_kt - 1) & 1) last_tile(cx, n_kt, acc, SB, PA, PB, ln, sel);
+  else last_tile(cx, n_kt, acc, SA, PB, PA, ln, sel);
   wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS past this point
 }
 
@@ -280,6 +398,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   }
   cx.seg_len = seg_len;
   cx.c = c;
+  cx.lazy = kLazyLog2 / c;
   const int n_kt = (seg_len + kBK - 1) / kBK;
 
   Lane ln;
@@ -287,30 +406,29 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   ln.h32 = ln.lane >> 5;
   ln.l32 = ln.lane & 31;
   // K rows: lane (key l32 of half a, h32) reads dims 64 c2 + 32 h32 .. +31, i.e. chunks
-  // 4 c2 + 2 h32 + sub of row 32 a + l32.
+  // 4 c2 + 2 h32 + sub of row 32 a + l32. The swizzle of row 32 a + l32 does not depend on a,
+  // so key half a is the immediate offset 32 a rows.
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int row = 32 * a + ln.l32;
-        const int chunk = 4 * c2 + 2 * ln.h32 + sub;
-        ln.kaddr[4 * a + 2 * c2 + sub] = lds_base + row * kRow8 + ((chunk ^ sw8(row)) << 4);
-      }
+    for (int sub = 0; sub < 2; ++sub) {
+      const int row = ln.l32;
+      const int chunk = 4 * c2 + 2 * ln.h32 + sub;
+      ln.kaddr[2 * c2 + sub] = lds_base + row * kRow8 + ((chunk ^ sw8(row)) << 4);
+    }
   // V^T (d-block db, read r): in 16-lane group (m0, h32) lane L gives the address of row
-  // key_of(h32, 8 r + L / 2), columns 32 db + m0 + 8 (L % 2) .. +7; the read returns to lane L
-  // column 32 db + m0 + L of those 8 rows.
+  // key_of(h32, 8 r + L / 2) = 16 r + 8 (L / 8) + 4 h32 + (L / 2) % 4, columns
+  // 32 db + m0 + 8 (L % 2) .. +7; the read returns to lane L column 32 db + m0 + L of those 8
+  // rows. The swizzle of that row does not depend on r, so read r is the immediate offset 16 r
+  // rows.
   {
     const int L = ln.lane & 15, m0 = 16 * ((ln.lane >> 4) & 1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = key_of(ln.h32, 8 * r + (L >> 1));
-        const int col = 32 * db + m0 + 8 * (L & 1);
-        ln.vaddr[4 * db + r] = lds_base + kRingBytes + row * kRow8 + (((col >> 4) ^ sw8(row)) << 4) + (col & 15);
-      }
+    for (int db = 0; db < 4; ++db) {
+      const int row = key_of(ln.h32, L >> 1);
+      const int col = 32 * db + m0 + 8 * (L & 1);
+      ln.vaddr[db] = lds_base + kRingBytes + row * kRow8 + (((col >> 4) ^ sw8(row)) << 4) + (col & 15);
+    }
   }
 
   // Q^T operand: lane (query l32, h32) holds dims 64 c2 + 32 h32 .. +31 for c2 = 0, 1.
@@ -330,16 +448,22 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       }
     }
   }
-  i32x8 ones;
+  // Selection operand of the weight-sum MFMA: lane (m = lane % 16, block lane / 16) is all
+  // e4m3 ones for m = 0 with an even block and m = 4 with an odd block, else zero.
+  i32x8 sel;
+  {
+    const int m = ln.lane & 15, blk = ln.lane >> 4;
+    const bool one = (m == 0 && !(blk & 1)) || (m == 4 && (blk & 1));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (int)kOnes;
+    for (int i = 0; i < 8; ++i) sel[i] = one ? (int)kOnes : 0;
+  }
 
   Acc acc;
-  run_online(cx, n_kt, acc, qr, ln, ones);
+  run(cx, n_kt, acc, qr, ln, sel);
 
   // O = dv (P V) / sum(P) -> bf16; LSE = (m c - 5 + log2 l) ln 2.
   const float l = pair_sum(acc.l);
-  const float lb = acc.LB[0];
+  const float lb = pair_sum(acc.LB[0]);  // lanes 32..63 hold 0
   const float mul = dv / lb;
   const int row = q0 + wave * 32 + ln.l32;
   if (row < seg_len) {
