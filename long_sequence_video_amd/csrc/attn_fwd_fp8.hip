@@ -29,9 +29,9 @@
 //    representable weight. A fixed
 //    first-tile reference, as in the BF16 kernel, would overflow e4m3's range whenever a
 //    later key exceeds the first tile by 3.8 log2 units, which long rows do routinely.
-//  * LDS: K and V rows of 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7),
-//    which keeps 16 consecutive rows (the row reads) and the 8 rows of a transposed read on
-//    distinct banks. K and V stream through an 8-slot ring, 4 tiles ahead, one barrier per tile.
+//  * LDS: K and V rows of 128 bytes with 16-byte chunk c of row r stored at c ^ sw8(r), a
+//    permutation of the row-pair index that keeps the row reads and the transposed reads free
+//    of bank conflicts. K and V stream through an 8-slot ring, 4 tiles ahead, one barrier per tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -65,7 +65,16 @@ constexpr float kLazyLog2 = 3.0f;         // raise the running max only beyond t
 constexpr unsigned kOnes = 0x38383838u;   // four e4m3 ones
 static_assert(kAhead >= 2 && kAhead <= kSlots - 2, "ring too small for the prefetch distance");
 
-__device__ __forceinline__ int sw8(int row) { return (row >> 1) & 7; }
+// Chunk swizzle of a row: with k = (row / 2) % 8 (rows 2k and 2k + 1 sit in the two halves of
+// the 64 banks), 4 (k % 2) + k / 2. Any 8 even (or odd) rows of a 16-row block get 8 distinct
+// values (row reads), and the row pairs of one transposed read, k in {0, 1, 4, 5} or
+// {2, 3, 6, 7}, get distinct value / 2, so the two 16-lane groups of a 32-lane half, which
+// read adjacent chunks of the same rows, meet no bank twice. A function of k only: rows 32 and
+// 16 apart share it (immediate read offsets).
+__device__ __forceinline__ int sw8(int row) {
+  const int k = (row >> 1) & 7;
+  return ((k & 1) << 2) | (k >> 1);
+}
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);

@@ -94,12 +94,13 @@ def test_fp8_dominant_late_key(gpu):
     compare_fp8(f8, out, lse, label="fp8 dominant")
 
 
-def _sampled(f8, n, seed):
+def _sampled(f8, n, seed, edge=128):
+    """The first and last ``edge`` query rows of every segment plus ``n`` random ones."""
     rng = np.random.default_rng(seed)
     rows = []
     for a, b in zip(f8.cu_seqlens[:-1], f8.cu_seqlens[1:]):
         if b > a:
-            rows += [np.arange(a, min(b, a + 128)), np.arange(max(a, b - 128), b), rng.integers(a, b, size=n)]
+            rows += [np.arange(a, min(b, a + edge)), np.arange(max(a, b - edge), b), rng.integers(a, b, size=n)]
     return np.unique(np.concatenate(rows))
 
 
@@ -116,7 +117,8 @@ def test_fp8_varlen_pack_sampled_and_deterministic(gpu):
     f8 = gen.make_fp8_config("varlen_19394_38000_104000_h56")
     say("case fp8 varlen pack")
     out, lse = run_fp8(f8, gpu)
-    compare_fp8(f8, out, lse, rows=_sampled(f8, 24, 8), label="fp8 varlen pack")
+    # 32-row edges keep the fp64 oracle on 161k tokens x 56 heads to about a minute
+    compare_fp8(f8, out, lse, rows=_sampled(f8, 24, 8, edge=32), label="fp8 varlen pack")
     out2, lse2 = run_fp8(f8, gpu)
     assert np.array_equal(out, out2) and np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
     torch.cuda.empty_cache()
