@@ -51,6 +51,7 @@ EXTRA_CONFIGS = {"h56_s104000": dict(seqlens=[104000], heads=56, seed=1005)}
 
 KERNEL_SOURCE = os.path.join(ROOT, "long_sequence_video_amd", "csrc", "attn_fwd.hip")
 PROLOGUE_SOURCE = os.path.join(ROOT, "long_sequence_video_amd", "csrc", "qkv_prologue.hip")
+FP8_SOURCE = os.path.join(ROOT, "long_sequence_video_amd", "csrc", "attn_fwd_fp8.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "{kernel}_{workload}_hbm_traffic.md")
 
 
@@ -171,12 +172,14 @@ def bench_fp8(name: str, steps: int, warmup: int):
     ms = e0.elapsed_time(e1) / steps
     tf = f8.flops() / (ms * 1e-3) / 1e12
     log(f"{name} fp8: {ms:.3f} ms, {tf:.1f} TFLOP/s, {100 * tf / PEAK_FP8_TFLOPS:.1f}% of the FP8 peak")
+    traffic, traffic_src = measured_traffic(name, kernel_source=FP8_SOURCE, kernel="attn_fwd_fp8")
     del q, k, v, out, lse
     torch.cuda.empty_cache()
     return {
         "workload": name + " (e4m3, per-tensor descales)", "ms_per_step": round(ms, 4), "steps": steps,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "kernel": "attn_fwd_fp8_kernel",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "traffic_source": traffic_src,
+                     "kernel": "attn_fwd_fp8_kernel",
                      # plus the weight-sum MFMA: half of a 32x32x64 per eight
                      "mfma_flops_executed": f8.flops() * (17.0 / 16.0)},
     }
