@@ -20,7 +20,7 @@
 //    accumulator's row order, and V^T is read from row-major V in LDS with
 //    ds_read_b64_tr_b16 in that same key order. No shuffles of P.
 //  * K and V tiles of 32 keys stream from global memory straight into an 8-slot LDS ring
-//    with 16-byte global_load_lds_dwordx4, four tiles ahead of use; one barrier per tile.
+//    with 16-byte global_load_lds_dwordx4, five tiles ahead of use; one barrier per two tiles.
 //    A tile's row offset is uniform (scalar base), so the copies cost no vector ALU; the
 //    last, partial tile of a segment is loaded shifted to end at the segment end, and its
 //    leading keys (already counted in the previous tile) are masked.
@@ -57,7 +57,7 @@ constexpr int kWaves = 8;                     // waves per workgroup
 constexpr int kBQ = kWaveQ * kWaves;          // query rows per workgroup
 constexpr int kBK = 32;                       // keys per tile
 constexpr int kSlots = 8;                     // LDS ring slots (K and V each)
-constexpr int kAhead = 4;                     // tiles in flight ahead of use
+constexpr int kAhead = 5;                     // tiles in flight ahead of use
 constexpr int kThreads = kWaves * 64;
 constexpr int kSlotBytes = kTileBytes;        // 8 KB: 32 key rows of 256 bytes
 constexpr int kRingBytes = kSlots * kSlotBytes;
@@ -66,7 +66,13 @@ constexpr int kCopies = kSlotBytes / 1024 / kWaves;  // 1 KB copies per wave per
 constexpr int kOpsPerTile = 2 * kCopies;             // memory instructions per wave per tile
 constexpr float kLazyLog2 = 8.0f;             // exact path: raise the running max only beyond this
 static_assert(kCopies == 1, "one 1 KB copy per wave per tile");
-static_assert(kAhead >= 2 && kAhead <= kSlots - 2, "ring too small for the prefetch distance");
+// The workgroup synchronises after odd tiles only. Between two barriers a wave runs at most
+// tiles t+1, t+2 (t odd) and copies tiles t+1+kAhead, t+2+kAhead, into the slots of tiles
+// t+1+kAhead-kSlots and t+2+kAhead-kSlots; a wave still behind has finished tile t, so it may
+// read V(t), K(t+2) (tile t+1) or V(t+1), K(t+3) (tile t+2): the written slots must be none
+// of tiles t .. t+3, i.e. kAhead <= kSlots - 3. Each barrier follows the wait for tile t+3
+// (read as K by tile t+2), leaving kAhead - 3 tiles in flight.
+static_assert(kAhead >= 3 && kAhead <= kSlots - 3, "ring too small for the prefetch distance");
 
 struct Lane {
   int lane, h32, l32;
@@ -198,8 +204,8 @@ __device__ __forceinline__ void softmax_all(const f32x16& S, bf16x8 (&P)[2], flo
 //   n = 0..7:  O += P(t-1) V(t-1)   (V operand n)
 //   n = 8..15: S(t+1) = Q K(t+1)^T  (K operand n - 8)
 // with each LDS operand read two MFMAs ahead, the eight exp2 pairs of S(t) after the odd
-// MFMAs, and the copy of tile t + kAhead after MFMA 4. Then tile t+2 is waited for and the
-// workgroup synchronises. No branches.
+// MFMAs, and the copy of tile t + kAhead after MFMA 4. After an odd tile, tile t+3 is waited
+// for and the workgroup synchronises. No branches.
 template <int U>
 __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const f32x16& Scur, f32x16& Snext,
                                           const bf16x8 (&Pprev)[2], bf16x8 (&Pcur)[2], float nmc,
@@ -230,8 +236,10 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
   Pcur[1] = __builtin_bit_cast(bf16x8, p[1]);
   // P(t) and the row sums must be complete here (they must not sink into the next tile).
   asm volatile("" : "+v"(Pcur[0]), "+v"(Pcur[1]), "+v"(acc.l), "+v"(acc.lb));
-  wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
-  barrier_lds();
+  if (U & 1) {
+    wait_vmcnt<kOpsPerTile * (kAhead - 3)>();
+    barrier_lds();
+  }
 }
 
 // Runs the whole key loop with a fixed per-row reference (the max of the first tile).
@@ -263,7 +271,7 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
   if (n_kt > 1) {
     SB = qk_tile(1 * kSlotBytes, qr, ln);
     load_tile(cx, kAhead);
-    wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
+    wait_vmcnt<kOpsPerTile * (kAhead - 3)>();  // as after an odd tile: tiles 2 and 3 are read next
     barrier_lds();
   }
 
