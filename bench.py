@@ -353,14 +353,17 @@ def main():
         step()
     torch.cuda.synchronize(dev)
     stream = torch.cuda.current_stream(dev)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # One event between consecutive launches: the first and last bracket the timed steps, and
+    # the ones in between give the per-launch distribution (p50 / p95).
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize(dev)
-    start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
-    end.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize(dev)
-    ms_per_step = start.elapsed_time(end) / args.steps
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     log(f"{args.config}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s, {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
 
@@ -392,6 +395,9 @@ def main():
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "step_ms": {"p50": round(float(np.percentile(per_step, 50)), 4),
+                    "p95": round(float(np.percentile(per_step, 95)), 4),
+                    "min": round(per_step[0], 4), "max": round(per_step[-1], 4)},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),

@@ -41,8 +41,9 @@ def build_library(verbose: bool = False) -> str:
     """Compile ``gen.c`` with gcc into ``liblsvgen.so`` (always recompiles)."""
     import subprocess
     tmp = LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11",
-           SOURCE_PATH, "-o", tmp, "-lm"]
+    include = os.path.join(os.path.dirname(os.path.dirname(_HERE)), "include")
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11", "-Wall", "-Werror",
+           "-I", include, SOURCE_PATH, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

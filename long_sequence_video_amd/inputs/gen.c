@@ -23,6 +23,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include "lsvgen.h"
+
 #define GAMMA 0x9E3779B97F4A7C15ULL
 
 static inline uint64_t mix64(uint64_t z) {

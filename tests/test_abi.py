@@ -29,6 +29,30 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+GEN_HEADER = os.path.join(ROOT, "include", "lsvgen.h")
+
+
+def test_generator_library_exports_every_declared_symbol():
+    from long_sequence_video_amd import inputs as gen
+    text = re.sub(r"/\*.*?\*/", "", open(GEN_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(lsvgen_\w+)\s*\(", text)))
+    assert names == ["lsvgen_choose", "lsvgen_normal_bf16", "lsvgen_normal_f64_at", "lsvgen_rms_normalize_bf16",
+                     "lsvgen_scale_rows_bf16"]
+    lib = ctypes.CDLL(gen.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_generator_rejects_bad_arguments():
+    from long_sequence_video_amd import inputs as gen
+    lib = ctypes.CDLL(gen.LIB_PATH)
+    assert lib.lsvgen_normal_bf16(None, ctypes.c_int64(-1), ctypes.c_uint64(1), ctypes.c_uint32(0)) == -1
+    assert lib.lsvgen_normal_bf16(None, ctypes.c_int64(4), ctypes.c_uint64(1), ctypes.c_uint32(0)) == -1
+    assert lib.lsvgen_normal_bf16(None, ctypes.c_int64(0), ctypes.c_uint64(1), ctypes.c_uint32(0)) == 0
+    assert lib.lsvgen_choose(None, ctypes.c_int64(3), ctypes.c_int64(2), None, ctypes.c_uint64(1),
+                             ctypes.c_uint32(3)) == -1
+
+
 def test_status_strings():
     assert lsv.lsv_status_string(0) == "ok"
     for code in (-1, -2, -3, -4, -5):
