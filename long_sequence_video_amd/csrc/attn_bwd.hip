@@ -282,7 +282,10 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) dq_load(cx, t);
   } else {
-    dq_load_short(cx);  // fewer copies in flight than the waits allow: they return early
+    dq_load_short(cx);
+    // One tile's copies are fewer than the steps' waits leave in flight, so those waits would
+    // not cover them: wait for them here (the step's barrier then publishes every wave's part).
+    wait_vmcnt<0>();
   }
   for (int t = 0; t < n_t; t += kSlots) {
     dq_step<0>(cx, ln, t, n_t, qr, dor, nl, dinit, c, acc);
@@ -499,6 +502,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int t = 0; t < kAhead; ++t) kv_load(cx, t, lane);
   } else {
     kv_load_short(cx, lane, wave);
+    // As in the dQ kernel: the steps' waits leave more copies in flight than one tile issues.
+    wait_vmcnt<0>();
   }
   for (int t = 0; t < n_t; t += kSlots) {
     kv_step<0>(cx, ln, t, n_t, kr, vr, c, dka, dva);
