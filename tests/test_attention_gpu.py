@@ -52,6 +52,16 @@ def test_ragged_varlen_all_rows(gpu, seqlens, heads):
     compare(inp, out, lse, label=f"ragged {seqlens} h{heads}")
 
 
+def test_many_single_tile_segments(gpu):
+    """96 segments shorter than one key tile (the short-copy path), every row compared."""
+    rng = np.random.default_rng(19)
+    seqlens = [int(x) for x in rng.integers(1, 32, size=96)]
+    inp = gen.generate(seqlens, 2, seed=319, name="short_segments")
+    say(f"case {len(seqlens)} short segments, {inp.total_tokens} tokens")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, label="short segments")
+
+
 def test_scale_values(gpu):
     for scale in (0.125, 0.02, 0.3):
         inp = gen.generate([300, 77], 2, seed=5, scale=scale, name="scale")

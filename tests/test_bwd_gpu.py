@@ -97,6 +97,19 @@ def test_ragged_all_rows(gpu, seqlens, heads):
     compare(inp, do, grads, label=f"bwd {seqlens} h{heads}")
 
 
+def test_many_single_tile_segments(gpu):
+    """Regression: segments shorter than one 32-row tile take the short-copy path, whose
+    copies must have landed before the first step reads them (an earlier build let the
+    step's wait return early). 96 such segments, every row compared."""
+    rng = np.random.default_rng(17)
+    seqlens = [int(x) for x in rng.integers(1, 32, size=96)]
+    inp = gen.generate(seqlens, 2, seed=317, name="bwd_short")
+    do = _dout(inp, 318)
+    say(f"case bwd {len(seqlens)} short segments, {inp.total_tokens} tokens")
+    grads = run_bwd(inp, do, gpu)
+    compare(inp, do, grads, label="bwd short segments")
+
+
 def test_rows_outside_segments_untouched(gpu):
     inp = gen.generate([100, 0, 61], 2, seed=12, total_tokens=200, name="poison")
     do = _dout(inp, 13)

@@ -72,6 +72,16 @@ def test_fp8_all_rows(gpu, seqlens, heads):
     compare_fp8(f8, out, lse, label=f"fp8 {seqlens} h{heads}")
 
 
+def test_fp8_many_single_tile_segments(gpu):
+    """96 segments shorter than one 64-key tile (the short-copy path), every row compared."""
+    rng = np.random.default_rng(23)
+    seqlens = [int(x) for x in rng.integers(1, 64, size=96)]
+    f8 = gen.quantize_fp8(gen.generate(seqlens, 2, seed=323, name="fp8_short"))
+    say(f"case fp8 {len(seqlens)} short segments")
+    out, lse = run_fp8(f8, gpu)
+    compare_fp8(f8, out, lse, label="fp8 short segments")
+
+
 def test_fp8_poison_outside_segments(gpu):
     f8 = gen.quantize_fp8(gen.generate([100, 0, 61], 2, seed=51, total_tokens=200, name="poison"))
     for t in (f8.q, f8.k, f8.v):
