@@ -256,6 +256,7 @@ __device__ __forceinline__ unsigned slot_of(int t) { return (unsigned)(t & (kSlo
 // P(t-1), with the weights P(t) of S(t) computed between them, operands read one MFMA
 // ahead and the copy of tile t + kAhead issued after the fifth.
 // Then tile t+2 is waited for and the workgroup synchronises.
+template <int U>
 __device__ __forceinline__ void step(const Ctx& cx, int t, Acc& acc, const f32x16 (&Scur)[2], f32x16 (&Snext)[2],
                                      const i32x8& Pprev, i32x8& Pcur, const i32x8 (&qr)[2], const Lane& ln,
                                      const i32x8& sel) {
@@ -269,7 +270,8 @@ __device__ __forceinline__ void step(const Ctx& cx, int t, Acc& acc, const f32x1
     acc.m = mnew;
   }
   const float nr = kRefLog2 - acc.m * cx.c;
-  const Bases b = bases(ln, slot_of(t + 1), slot_of(t - 1));
+  // t % kSlots == U: both ring slots are compile-time offsets (LDS read immediates).
+  const Bases b = bases(ln, ((U + 1) % kSlots) * kSlot, ((U + kSlots - 1) % kSlots) * kSlot);
   i32x8 opnd[9];
   auto read = [&](int n) {
     if (n < 4) opnd[n] = k_operand(b, n >> 1, n & 1);
@@ -360,11 +362,24 @@ __device__ __forceinline__ void run(const Ctx& cx, int n_kt, Acc& acc, const i32
 
   const int last = n_kt - 2;
   int t = 1;
-  for (; t + 1 <= last; t += 2) {
-    step(cx, t, acc, SB, SA, PA, PB, qr, ln, sel);
-    step(cx, t + 1, acc, SA, SB, PB, PA, qr, ln, sel);
+  // Eight tiles per iteration (ring slots 1..7, 0), then up to seven more.
+  for (; t + 7 <= last; t += 8) {
+    step<1>(cx, t + 0, acc, SB, SA, PA, PB, qr, ln, sel);
+    step<2>(cx, t + 1, acc, SA, SB, PB, PA, qr, ln, sel);
+    step<3>(cx, t + 2, acc, SB, SA, PA, PB, qr, ln, sel);
+    step<4>(cx, t + 3, acc, SA, SB, PB, PA, qr, ln, sel);
+    step<5>(cx, t + 4, acc, SB, SA, PA, PB, qr, ln, sel);
+    step<6>(cx, t + 5, acc, SA, SB, PB, PA, qr, ln, sel);
+    step<7>(cx, t + 6, acc, SB, SA, PA, PB, qr, ln, sel);
+    step<0>(cx, t + 7, acc, SA, SB, PB, PA, qr, ln, sel);
   }
-  if (t <= last) step(cx, t, acc, SB, SA, PA, PB, qr, ln, sel);
+  if (t <= last) step<1>(cx, t, acc, SB, SA, PA, PB, qr, ln, sel);
+  if (t + 1 <= last) step<2>(cx, t + 1, acc, SA, SB, PB, PA, qr, ln, sel);
+  if (t + 2 <= last) step<3>(cx, t + 2, acc, SB, SA, PA, PB, qr, ln, sel);
+  if (t + 3 <= last) step<4>(cx, t + 3, acc, SA, SB, PB, PA, qr, ln, sel);
+  if (t + 4 <= last) step<5>(cx, t + 4, acc, SB, SA, PA, PB, qr, ln, sel);
+  if (t + 5 <= last) step<6>(cx, t + 5, acc, SA, SB, PB, PA, qr, ln, sel);
+  if (t + 6 <= last) step<7>(cx, t + 6, acc, SB, SA, PA, PB, qr, ln, sel);
   if ((n_kt - 1) & 1) last_tile(cx, n_kt, acc, SB, PA, PB, ln, sel);
   else last_tile(cx, n_kt, acc, SA, PB, PA, ln, sel);
   wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS past this point
