@@ -226,6 +226,22 @@ def test_c5_varlen_and_segment_isolation(gpu):
     torch.cuda.empty_cache()
 
 
+def test_largest_supported_segment(gpu):
+    """One segment of 299,593 tokens x 56 heads: the largest the 32-bit in-segment copy
+    offsets allow (max_seqlen * heads * 256 + 256 < 2^32; one token more is rejected on the
+    host). Sampled rows, including the first and last query tiles, against the oracle."""
+    import torch
+    n = 299_593
+    assert n * 56 * 256 + 256 < 2 ** 32 <= (n + 1) * 56 * 256 + 256
+    _cache.clear()
+    inp = gen.generate([n], 56, seed=1006, name="max_segment_s299593_h56")
+    say("case max segment 299593 x 56")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, rows=sample_rows(inp, 16, seed=6, tile=32), label="max_segment_s299593_h56")
+    del inp, out, lse
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- dynamic range (exact fallback)
 
 
