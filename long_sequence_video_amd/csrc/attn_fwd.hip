@@ -33,7 +33,9 @@
 //  * Software pipeline per key tile t: one sequence of 16 MFMAs (O += P(t-1) V(t-1), then
 //    S(t+1) = Q K(t+1)^T) with the exp2 work of S(t) placed between them (explicit
 //    scheduling barriers hold the order); the steady-state loop body is branch-free.
-//  * P V uses p rounded to bf16 and O is divided by the sum of those same rounded p; the
+//  * P V uses p rounded to bf16 and O is divided by the sum of those same rounded p (on the
+//    fast path from two small selection MFMAs per tile, which keeps it off the vector ALU:
+//    the loop runs at the chip's power limit, so vector work costs matrix issue); the
 //    LSE uses the sum of the fp32 p.
 //  * LDS: K rows are XOR-swizzled in 16-byte chunks (conflict-free 32-row reads of one
 //    chunk); V 4-row blocks are stored column-block first (conflict-free transposing reads,
@@ -101,7 +103,16 @@ struct Acc {
   float m;      // reference max (raw score units)
   float l;      // sum of fp32 p: for the LSE
   float lb;     // sum of bf16(p), the weights P V used: normalises O
+  f32x4 LBm;    // fast path: element 0 of lanes 0..31 = sum of bf16(p) of query l32
 };
+
+// Row sums of bf16 P: one v_mfma_f32_16x16x32_bf16 per P operand whose A selects, for output
+// row 0, the lanes of queries 0..15 (lane blocks 0 and 2 of B) and, for row 4, those of
+// queries 16..31 (blocks 1 and 3). Row 0 lands in element 0 of lanes 0..15 and row 4 in
+// element 0 of lanes 16..31: each sum in the lane whose l32 is its query (lanes 32..63 get 0).
+__device__ __forceinline__ f32x4 mfma_rowsum(const bf16x8& sel, const bf16x8& p, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p, c, 0, 0, 0);
+}
 
 // Tile copies. Wave w copies rows 4w .. 4w+3 of the 32-row tile of K and of V (1 KB
 // apiece) into the ring slot at byte offset `slot`; lane i writes 16-byte slot i of that
@@ -174,8 +185,10 @@ __device__ __forceinline__ float lane_max(const f32x16& S) {
   return fmaxf(mx, S[15]);
 }
 
-// Scores 2j, 2j+1: p = exp2(s c - m c) -> bf16 pair into P; row sums of the fp32 p (l)
-// and of the bf16 p (lb, v_dot2_f32_bf16).
+// Scores 2j, 2j+1: p = exp2(s c - m c) -> bf16 pair into P; row sum of the fp32 p (l) and,
+// on the exact path (kLb), of the bf16 p (lb, v_dot2_f32_bf16). The fast path sums the bf16 p
+// with row-sum MFMAs instead (mfma_rowsum), off the vector ALU.
+template <bool kLb = true>
 __device__ __forceinline__ void softmax_pair(const f32x16& S, u32x4 (&P)[2], float& l, float& lb, float c,
                                              float nmc, int j) {
   const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * j], c, nmc));
@@ -187,15 +200,16 @@ __device__ __forceinline__ void softmax_pair(const f32x16& S, u32x4 (&P)[2], flo
   pp[1] = (__bf16)e1;
   one[0] = (__bf16)1.0f;
   one[1] = (__bf16)1.0f;
-  lb = __builtin_amdgcn_fdot2_f32_bf16(pp, one, lb, false);
+  if (kLb) lb = __builtin_amdgcn_fdot2_f32_bf16(pp, one, lb, false);
   P[j >> 2][j & 3] = __builtin_bit_cast(unsigned, pp);
 }
 
+template <bool kLb = true>
 __device__ __forceinline__ void softmax_all(const f32x16& S, bf16x8 (&P)[2], float& l, float& lb, float c,
                                             float nmc) {
   u32x4 p[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) softmax_pair(S, p, l, lb, c, nmc, j);
+  for (int j = 0; j < 8; ++j) softmax_pair<kLb>(S, p, l, lb, c, nmc, j);
   P[0] = __builtin_bit_cast(bf16x8, p[0]);
   P[1] = __builtin_bit_cast(bf16x8, p[1]);
 }
@@ -211,7 +225,7 @@ __device__ __forceinline__ void softmax_all(const f32x16& S, bf16x8 (&P)[2], flo
 template <int U>
 __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const f32x16& Scur, f32x16& Snext,
                                           const bf16x8 (&Pprev)[2], bf16x8 (&Pcur)[2], float nmc,
-                                          const bf16x8 (&qr)[8], const Lane& ln) {
+                                          const bf16x8 (&qr)[8], const Lane& ln, const bf16x8& sel) {
   constexpr unsigned vslot = ((U + kSlots - 1) % kSlots) * kSlotBytes;
   constexpr unsigned kslot = ((U + 1) % kSlots) * kSlotBytes;
   bf16x8 opnd[16];
@@ -230,7 +244,11 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
     else S = mfma(opnd[n], qr[n - 8], S);
     if (n + 2 < 16) read(n + 2);
     if (n == 4) load_tile(cx, t + kAhead);
-    if (n & 1) softmax_pair(Scur, p, acc.l, acc.lb, cx.c, nmc, n >> 1);
+    if (n == 7) {
+      acc.LBm = mfma_rowsum(sel, Pprev[0], acc.LBm);
+      acc.LBm = mfma_rowsum(sel, Pprev[1], acc.LBm);
+    }
+    if (n & 1) softmax_pair<false>(Scur, p, acc.l, acc.lb, cx.c, nmc, n >> 1);
     sched_fence();
   }
   Snext = S;
@@ -246,8 +264,13 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
 
 // Runs the whole key loop with a fixed per-row reference (the max of the first tile).
 // Returns false when this lane's sums or O are not finite (a p overflowed).
+__device__ __forceinline__ void lb_tile(Acc& acc, const bf16x8& sel, const bf16x8 (&P)[2]) {
+  acc.LBm = mfma_rowsum(sel, P[0], acc.LBm);
+  acc.LBm = mfma_rowsum(sel, P[1], acc.LBm);
+}
+
 __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, const bf16x8 (&qr)[8],
-                                         const Lane& ln) {
+                                         const Lane& ln, const bf16x8& sel) {
   if (n_kt >= 2) {
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) load_tile(cx, t);
@@ -261,6 +284,7 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
   for (int db = 0; db < 4; ++db) acc.O[db] = f32x16{};
   acc.l = 0.f;
   acc.lb = 0.f;
+  acc.LBm = f32x4{};
   f32x16 SA, SB;
   bf16x8 PA[2], PB[2];
 
@@ -269,7 +293,7 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
   if (n_kt == 1) mask_tail(SA, cx.seg_len, ln);
   acc.m = pair_max(lane_max(SA));
   const float nmc = -acc.m * cx.c;
-  softmax_all(SA, PA, acc.l, acc.lb, cx.c, nmc);
+  softmax_all<false>(SA, PA, acc.l, acc.lb, cx.c, nmc);
   if (n_kt > 1) {
     SB = qk_tile(1 * kSlotBytes, qr, ln);
     load_tile(cx, kAhead);
@@ -282,22 +306,22 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
   const int last = n_kt - 2;
   int t = 1;
   for (; t + 7 <= last; t += 8) {
-    fast_step<1>(cx, t + 0, acc, SB, SA, PA, PB, nmc, qr, ln);
-    fast_step<2>(cx, t + 1, acc, SA, SB, PB, PA, nmc, qr, ln);
-    fast_step<3>(cx, t + 2, acc, SB, SA, PA, PB, nmc, qr, ln);
-    fast_step<4>(cx, t + 3, acc, SA, SB, PB, PA, nmc, qr, ln);
-    fast_step<5>(cx, t + 4, acc, SB, SA, PA, PB, nmc, qr, ln);
-    fast_step<6>(cx, t + 5, acc, SA, SB, PB, PA, nmc, qr, ln);
-    fast_step<7>(cx, t + 6, acc, SB, SA, PA, PB, nmc, qr, ln);
-    fast_step<0>(cx, t + 7, acc, SA, SB, PB, PA, nmc, qr, ln);
+    fast_step<1>(cx, t + 0, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
+    fast_step<2>(cx, t + 1, acc, SA, SB, PB, PA, nmc, qr, ln, sel);
+    fast_step<3>(cx, t + 2, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
+    fast_step<4>(cx, t + 3, acc, SA, SB, PB, PA, nmc, qr, ln, sel);
+    fast_step<5>(cx, t + 4, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
+    fast_step<6>(cx, t + 5, acc, SA, SB, PB, PA, nmc, qr, ln, sel);
+    fast_step<7>(cx, t + 6, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
+    fast_step<0>(cx, t + 7, acc, SA, SB, PB, PA, nmc, qr, ln, sel);
   }
-  if (t <= last) fast_step<1>(cx, t, acc, SB, SA, PA, PB, nmc, qr, ln);
-  if (t + 1 <= last) fast_step<2>(cx, t + 1, acc, SA, SB, PB, PA, nmc, qr, ln);
-  if (t + 2 <= last) fast_step<3>(cx, t + 2, acc, SB, SA, PA, PB, nmc, qr, ln);
-  if (t + 3 <= last) fast_step<4>(cx, t + 3, acc, SA, SB, PB, PA, nmc, qr, ln);
-  if (t + 4 <= last) fast_step<5>(cx, t + 4, acc, SB, SA, PA, PB, nmc, qr, ln);
-  if (t + 5 <= last) fast_step<6>(cx, t + 5, acc, SA, SB, PB, PA, nmc, qr, ln);
-  if (t + 6 <= last) fast_step<7>(cx, t + 6, acc, SB, SA, PA, PB, nmc, qr, ln);
+  if (t <= last) fast_step<1>(cx, t, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
+  if (t + 1 <= last) fast_step<2>(cx, t + 1, acc, SA, SB, PB, PA, nmc, qr, ln, sel);
+  if (t + 2 <= last) fast_step<3>(cx, t + 2, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
+  if (t + 3 <= last) fast_step<4>(cx, t + 3, acc, SA, SB, PB, PA, nmc, qr, ln, sel);
+  if (t + 4 <= last) fast_step<5>(cx, t + 4, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
+  if (t + 5 <= last) fast_step<6>(cx, t + 5, acc, SA, SB, PB, PA, nmc, qr, ln, sel);
+  if (t + 6 <= last) fast_step<7>(cx, t + 6, acc, SB, SA, PA, PB, nmc, qr, ln, sel);
 
   // Last tile (n_kt >= 2): P V of tile n_kt-2, masked exp2 of the shifted tile n_kt-1, its P V.
   const int tl = n_kt - 1;
@@ -307,18 +331,24 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
     const int skip = kBK - (cx.seg_len - tl * kBK);
     if (tl & 1) {
       pv_tile(acc.O, vprev, PA, ln);
+      lb_tile(acc, sel, PA);
       mask_head(SB, skip, ln);
-      softmax_all(SB, PB, acc.l, acc.lb, cx.c, nmc);
+      softmax_all<false>(SB, PB, acc.l, acc.lb, cx.c, nmc);
       pv_tile(acc.O, vlast, PB, ln);
+      lb_tile(acc, sel, PB);
     } else {
       pv_tile(acc.O, vprev, PB, ln);
+      lb_tile(acc, sel, PB);
       mask_head(SA, skip, ln);
-      softmax_all(SA, PA, acc.l, acc.lb, cx.c, nmc);
+      softmax_all<false>(SA, PA, acc.l, acc.lb, cx.c, nmc);
       pv_tile(acc.O, vlast, PA, ln);
+      lb_tile(acc, sel, PA);
     }
   } else {
     pv_tile(acc.O, 0, PA, ln);
+    lb_tile(acc, sel, PA);
   }
+  acc.lb = acc.LBm[0];  // lanes 32..63 hold 0: the epilogue's pair sum is the row's sum
   // No copy may still be writing this workgroup's LDS past this point.
   wait_vmcnt<0>();
   float big = fmaxf(fabsf(acc.l), fabsf(acc.lb));
@@ -434,7 +464,14 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   }
 
   Acc acc;
-  const bool ok = run_fast(cx, n_kt, acc, qr, ln);
+  bf16x8 sel;
+  {
+    const int m = ln.lane & 15, blk = ln.lane >> 4;
+    const bool one = (m == 0 && !(blk & 1)) || (m == 4 && (blk & 1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sel[i] = one ? (__bf16)1.0f : (__bf16)0.0f;
+  }
+  const bool ok = run_fast(cx, n_kt, acc, qr, ln, sel);
   // Workgroup-wide verdict: any overflowing row sends the whole workgroup down the exact path.
   lds_int* flags = (lds_int*)(uintptr_t)(lds_base + 2 * kRingBytes);
   if (tid < kWaves) flags[tid] = 0;
