@@ -91,8 +91,7 @@ __device__ __forceinline__ void pack_pair(u32x4 (&P)[2], int j, float a, float b
 }
 
 // Workgroup -> (head, segment, 256-row tile), XCD-aware: hardware dispatches block b to XCD
-// b % 8; each XCD gets a contiguous range of logical tiles (head-major, then segment, longest
-// segment first within a head).
+// b % 8; each XCD gets a contiguous range of logical tiles (head-major, then segment).
 struct Work {
   int head, seg_start, seg_len, r0;
   bool ok;
@@ -106,7 +105,7 @@ __device__ __forceinline__ Work map_block(const int32_t* cu_seqlens, int n_seqs,
   if (logical >= n_logical) return w;
   const int rt = logical % tiles_per_seq;
   const int hs = logical / tiles_per_seq;
-  const int seg = segment_of_rank(cu_seqlens, n_seqs, hs % n_seqs);
+  const int seg = hs % n_seqs;
   w.head = hs / n_seqs;
   w.seg_start = cu_seqlens[seg];
   const int seg_end = cu_seqlens[seg + 1];

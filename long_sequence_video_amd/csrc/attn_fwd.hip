@@ -42,8 +42,7 @@
 //    and every V read address is one lane base plus an immediate).
 //  * Workgroups are remapped so that consecutive tiles of one (head, segment) land on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2; each XCD's range is
-//    head-major (heads spread evenly over the XCDs), and within a head the longest segment
-//    goes first, so every XCD's queue ends on short tiles.
+//    head-major (heads spread evenly over the XCDs), segments in packed order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -409,14 +408,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
 
   // XCD-aware order: hardware dispatches block b to XCD b % 8; give each XCD a contiguous
-  // range of logical tiles (head-major, then segment, longest first within a head, then
-  // query tile).
+  // range of logical tiles (head-major, then segment in packed order, then query tile).
   const int per_xcd = gridDim.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (logical >= n_logical) return;
   const int qt = logical % tiles_per_seq;
   const int hs = logical / tiles_per_seq;
-  const int seg = segment_of_rank(cu_seqlens, n_seqs, hs % n_seqs);
+  const int seg = hs % n_seqs;
   const int head = hs / n_seqs;
   const int seg_start = cu_seqlens[seg];
   const int seg_end = cu_seqlens[seg + 1];

@@ -391,14 +391,13 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
                     int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
                     float dv, int n_logical) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
-  // XCD-aware order, as in the BF16 kernel: head-major ranges per XCD, longest segment first
-  // within a head.
+  // XCD-aware order, as in the BF16 kernel: head-major ranges per XCD.
   const int per_xcd = gridDim.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (logical >= n_logical) return;
   const int qt = logical % tiles_per_seq;
   const int hs = logical / tiles_per_seq;
-  const int seg = segment_of_rank(cu_seqlens, n_seqs, hs % n_seqs);
+  const int seg = hs % n_seqs;
   const int head = hs / n_seqs;
   const int seg_start = cu_seqlens[seg];
   const int seg_end = cu_seqlens[seg + 1];

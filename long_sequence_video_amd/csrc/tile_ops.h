@@ -135,23 +135,4 @@ __device__ __forceinline__ bf16x8 tr_operand(unsigned base, unsigned slot, int i
   return lds_tr(a, a + 2048);
 }
 
-// Work order of a packed batch: within each head, segments are visited longest first, so
-// a workgroup queue ends on short tiles rather than on the longest segment's. Returns the
-// index of the segment whose length has rank r (0 = longest; equal lengths in index order).
-// Each lane holds one segment's length; up to kRankedSegs segments are ranked, larger packs
-// keep their given order. Call with the whole wave active; the result is wave-uniform.
-constexpr int kRankedSegs = 16;
-__device__ __forceinline__ int segment_of_rank(const int32_t* cu_seqlens, int n_seqs, int r) {
-  if (n_seqs > kRankedSegs) return r;
-  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  const int len = lane < n_seqs ? cu_seqlens[lane + 1] - cu_seqlens[lane] : -1;
-  int rank = 0;
-  for (int j = 0; j < n_seqs; ++j) {
-    const int lj = __builtin_amdgcn_readlane(len, j);
-    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
-  }
-  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n_seqs && rank == r);
-  return hit ? (int)__builtin_ctzll(hit) : r;
-}
-
 }  // namespace lsv_tiles
