@@ -98,6 +98,20 @@ def test_empty_inputs_are_noops(gpu):
     assert bool((out == 3.0).all()) and bool((lse == 5.0).all())
 
 
+def test_max_seqlen_contract(gpu):
+    """max_seqlen only sizes the grid: a larger one gives bit-identical results, and a segment
+    longer than it is skipped (its rows untouched) while the others are unchanged."""
+    inp = gen.generate([300, 77, 150], 2, seed=16, name="max_seqlen")
+    say("case max_seqlen contract")
+    out, lse = run_kernel(inp, gpu)
+    out2, lse2 = run_kernel(inp, gpu, max_seqlen=1000)
+    assert np.array_equal(out, out2) and np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
+    out3, lse3 = run_kernel(inp, gpu, max_seqlen=160, out_fill=0x1234, lse_fill=-7.0)
+    assert np.all(out3[:300] == 0x1234) and np.all(lse3[:, :300] == -7.0)
+    assert np.array_equal(out3[300:], out[300:]) and np.array_equal(lse3[:, 300:].view(np.uint32),
+                                                                      lse[:, 300:].view(np.uint32))
+
+
 def test_unsupported_head_dim_raises(gpu):
     """The pages' own interface example uses head_dim 8; this library supports 128 only."""
     import torch

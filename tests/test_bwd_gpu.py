@@ -30,7 +30,7 @@ def _dout(inp, seed):
     return gen.normal_bf16(inp.q.size, seed, 9).reshape(inp.q.shape)
 
 
-def run_bwd(inp, do, device, *, out_bits=None, lse=None, fill=None):
+def run_bwd(inp, do, device, *, out_bits=None, lse=None, fill=None, max_seqlen=None):
     """Runs the HIP backward; O / LSE from the oracle's forward unless given."""
     import torch
     import long_sequence_video_amd as lsv
@@ -51,7 +51,8 @@ def run_bwd(inp, do, device, *, out_bits=None, lse=None, fill=None):
     if fill is not None:
         for g in grads:
             g.view(torch.int16).fill_(int(np.int16(np.uint16(fill))))
-    lsv.attn_bwd(q, k, v, o_d, do_d, lse_d, cu, inp.max_seqlen, inp.scale, dq=grads[0], dk=grads[1], dv=grads[2])
+    ms = inp.max_seqlen if max_seqlen is None else max_seqlen
+    lsv.attn_bwd(q, k, v, o_d, do_d, lse_d, cu, ms, inp.scale, dq=grads[0], dk=grads[1], dv=grads[2])
     torch.cuda.synchronize(device)
     return tuple(from_dev(g) for g in grads)
 
@@ -120,6 +121,21 @@ def test_rows_outside_segments_untouched(gpu):
     for g in grads:
         assert np.all(g[161:] == 0x1234)
     compare(inp, do, tuple(g[:161] for g in grads), label="bwd poison")
+
+
+def test_max_seqlen_contract(gpu):
+    """max_seqlen only sizes the grid: a larger one gives bit-identical gradients, and a
+    segment longer than it is skipped (its rows untouched) while the others are unchanged."""
+    inp = gen.generate([300, 77, 150], 2, seed=14, name="bwd_max_seqlen")
+    do = _dout(inp, 15)
+    say("case bwd max_seqlen contract")
+    exact = run_bwd(inp, do, gpu)
+    over = run_bwd(inp, do, gpu, max_seqlen=1000)
+    assert all(np.array_equal(a, b) for a, b in zip(exact, over))
+    short = run_bwd(inp, do, gpu, max_seqlen=160, fill=0x1234)
+    for g, e in zip(short, exact):
+        assert np.all(g[:300] == 0x1234)
+        assert np.array_equal(g[300:], e[300:])
 
 
 def test_identical_keys(gpu):

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 O_MAX, O_MEAN, LSE_MAX = 0.2, 1e-2, 2e-3
 
 
-def run_fp8(f8, device, *, out_fill=None):
+def run_fp8(f8, device, *, out_fill=None, max_seqlen=None):
     import torch
     import long_sequence_video_amd as lsv
     q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in (f8.q, f8.k, f8.v))
@@ -33,8 +33,8 @@ def run_fp8(f8, device, *, out_fill=None):
     if out_fill is not None:
         out.view(torch.int16).fill_(int(np.int16(np.uint16(out_fill))))
         lse.fill_(-7.0)
-    lsv.attn_fwd_fp8(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale, out=out,
-                     lse=lse)
+    ms = f8.max_seqlen if max_seqlen is None else max_seqlen
+    lsv.attn_fwd_fp8(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, ms, f8.scale, out=out, lse=lse)
     torch.cuda.synchronize(device)
     return from_dev(out), lse.cpu().numpy()
 
@@ -90,6 +90,20 @@ def test_fp8_poison_outside_segments(gpu):
     out, lse = run_fp8(f8, gpu, out_fill=0x1234)
     assert np.all(out[161:] == 0x1234) and np.all(lse[:, 161:] == -7.0)
     compare_fp8(f8, out, lse, rows=np.arange(161), label="fp8 poison")
+
+
+def test_fp8_max_seqlen_contract(gpu):
+    """As for the BF16 forward: a larger max_seqlen gives bit-identical results, and a segment
+    longer than it is skipped while the others are unchanged."""
+    f8 = gen.quantize_fp8(gen.generate([300, 77, 150], 2, seed=53, name="fp8_max_seqlen"))
+    say("case fp8 max_seqlen contract")
+    out, lse = run_fp8(f8, gpu)
+    out2, lse2 = run_fp8(f8, gpu, max_seqlen=1000)
+    assert np.array_equal(out, out2) and np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
+    out3, lse3 = run_fp8(f8, gpu, out_fill=0x1234, max_seqlen=160)
+    assert np.all(out3[:300] == 0x1234) and np.all(lse3[:, :300] == -7.0)
+    assert np.array_equal(out3[300:], out[300:]) and np.array_equal(lse3[:, 300:].view(np.uint32),
+                                                                      lse[:, 300:].view(np.uint32))
 
 
 def test_fp8_dominant_late_key(gpu):
