@@ -30,9 +30,10 @@
 //    unless p overflows, and then the row sums become non-finite. So the steady state
 //    carries no max tracking and no O rescale. If any row of the workgroup overflowed, the
 //    workgroup recomputes its tile with an exact online softmax (running max, O rescale).
-//  * Software pipeline per key tile t: one sequence of 16 MFMAs (O += P(t-1) V(t-1), then
-//    S(t+1) = Q K(t+1)^T) with the exp2 work of S(t) placed between them (explicit
-//    scheduling barriers hold the order); the steady-state loop body is branch-free.
+//  * Software pipeline per key tile t: one sequence of 18 MFMAs (O += P(t-1) V(t-1), the two
+//    row-sum MFMAs of P(t-1), then S(t+1) = Q K(t+1)^T) with the exp2 work of S(t) placed
+//    between them (explicit scheduling barriers hold the order); the steady-state loop body
+//    is branch-free.
 //  * P V uses p rounded to bf16 and O is divided by the sum of those same rounded p (on the
 //    fast path from two small selection MFMAs per tile, which keeps it off the vector ALU:
 //    the loop runs at the chip's power limit, so vector work costs matrix issue); the
@@ -216,7 +217,8 @@ __device__ __forceinline__ void softmax_all(const f32x16& S, bf16x8 (&P)[2], flo
 // ---------------------------------------------------------------------------- fast path
 
 // Steady-state tile t (1 <= t <= n_kt - 2, t % kSlots == U): one sequence of 16 MFMAs,
-//   n = 0..7:  O += P(t-1) V(t-1)   (V operand n)
+//   n = 0..7:  O += P(t-1) V(t-1)   (V operand n), then after n = 7 the two row-sum MFMAs
+//              of P(t-1)
 //   n = 8..15: S(t+1) = Q K(t+1)^T  (K operand n - 8)
 // with each LDS operand read two MFMAs ahead, the eight exp2 pairs of S(t) after the odd
 // MFMAs, and the copy of tile t + kAhead after MFMA 4. After an odd tile, tile t+3 is waited
