@@ -112,6 +112,21 @@ def test_max_seqlen_contract(gpu):
                                                                       lse[:, 300:].view(np.uint32))
 
 
+def test_malformed_segments_are_skipped(gpu):
+    """Segments that break the cu_seqlens contract are skipped inside the kernel: a negative
+    start, an end past total_tokens and an end before the start. The valid segment among them
+    is computed as usual, and every other row keeps its contents."""
+    base = gen.generate([400], 2, seed=17, name="malformed")
+    cu = np.array([-5, 50, 170, 600, 300], dtype=np.int32)
+    bad = gen.Inputs("malformed", base.q, base.k, base.v, cu, base.scale)
+    say("case malformed cu_seqlens")
+    out, lse = run_kernel(bad, gpu, out_fill=0x1234, lse_fill=-7.0, max_seqlen=1000)
+    keep = np.r_[0:50, 170:400]
+    assert np.all(out[keep] == 0x1234) and np.all(lse[:, keep] == -7.0)
+    ok = gen.Inputs("malformed_ok", base.q, base.k, base.v, np.array([0, 50, 170], np.int32), base.scale)
+    compare(ok, out, lse, rows=np.arange(50, 170), label="malformed: valid segment")
+
+
 def test_unsupported_head_dim_raises(gpu):
     """The pages' own interface example uses head_dim 8; this library supports 128 only."""
     import torch

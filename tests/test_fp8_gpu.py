@@ -106,6 +106,22 @@ def test_fp8_max_seqlen_contract(gpu):
                                                                       lse[:, 300:].view(np.uint32))
 
 
+def test_fp8_malformed_segments_are_skipped(gpu):
+    """As for the BF16 forward: a negative start, an end past total_tokens and an end before
+    the start are skipped; the valid segment is computed and every other row keeps its
+    contents."""
+    f8 = gen.quantize_fp8(gen.generate([400], 2, seed=54, name="fp8_malformed"))
+    good_cu = f8.cu_seqlens
+    f8.cu_seqlens = np.array([-5, 50, 170, 600, 300], dtype=np.int32)
+    say("case fp8 malformed cu_seqlens")
+    out, lse = run_fp8(f8, gpu, out_fill=0x1234, max_seqlen=1000)
+    keep = np.r_[0:50, 170:400]
+    assert np.all(out[keep] == 0x1234) and np.all(lse[:, keep] == -7.0)
+    f8.cu_seqlens = np.array([0, 50, 170], dtype=np.int32)
+    compare_fp8(f8, out, lse, rows=np.arange(50, 170), label="fp8 malformed: valid segment")
+    f8.cu_seqlens = good_cu
+
+
 def test_fp8_dominant_late_key(gpu):
     """A late key 12-16 log2 units above the first tile raises the running max (a weight
     against the old max would overflow e4m3, which has no infinity)."""
