@@ -213,19 +213,18 @@ def _config(name):
 
 def test_c2_boosted_keys(gpu):
     inp = _config("s4096_h56_kboost")
-    say("case s4096_h56_kboost")
+    say("case s4096_h56_kboost (every row)")
     out, lse = run_kernel(inp, gpu)
-    rows = sample_rows(inp, 384, seed=2)
-    compare(inp, out, lse, rows=rows, label="s4096_h56_kboost")
+    compare(inp, out, lse, label="s4096_h56_kboost")
     # every row is finite
     assert np.isfinite(bf16_bits_to_f64(out)).all() and np.isfinite(lse).all()
 
 
 def test_c3_sp4_share(gpu):
     inp = _config("sp4_share_s19394_h14")
-    say("case sp4_share_s19394_h14")
+    say("case sp4_share_s19394_h14 (every row)")
     out, lse = run_kernel(inp, gpu)
-    compare(inp, out, lse, rows=sample_rows(inp, 256, seed=3), label="sp4_share_s19394_h14")
+    compare(inp, out, lse, label="sp4_share_s19394_h14")
 
 
 def test_c4_h3_38000(gpu):

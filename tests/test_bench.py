@@ -1,0 +1,48 @@
+"""bench.py's output contract: one JSON line with the required fields (GPU), the refusal of
+more than one GPU and the CPU-baseline leg (CPU)."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_cpu_baseline_leg_reports_the_oracle_on_host_cores():
+    sys.path.insert(0, ROOT)
+    import bench
+    from long_sequence_video_amd import inputs as gen
+    res = bench.cpu_baseline(gen.make_config("tiny_s256_h4"), target_seconds=0.2)
+    assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s"
+    assert res["value"] > 0 and res["cores"] >= 1 and res["sample"]
+
+
+@pytest.mark.gpu
+def test_bench_json_line(gpu):
+    cmd = [sys.executable, BENCH, "--config", "tiny_s256_h4", "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+           "--no-prologue", "--no-bwd", "--no-fp8"]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+                "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["steps"] == 3 and line["warmup"] == 1
+    assert line["value"] > 0 and line["ms_per_step"] > 0 and line["higher_is_better"] is True
+    assert line["dtype"] == "bf16" and line["unit"] == "TFLOP/s"
+    assert line["config"]["workload"] == "tiny_s256_h4"
+    roof = line["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    assert roof["bound"] == "mfma" and roof["peak"] == 2500.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
