@@ -7,6 +7,7 @@ per step). Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
                   [--no-prologue] [--prologue-only] [--no-bwd] [--bwd-only] [--no-fp8] [--fp8-only]
+                  [--no-gemm-ref] [--gemm-ref-only]
   python bench.py --copy-bytes N   # a plain device copy of N bytes, to calibrate HBM counters
 
 An object ``attn_fwd_fp8`` times the FP8 (e4m3) forward on the same pack quantised per tensor,
@@ -22,6 +23,11 @@ A second object, ``qkv_prologue``, times the fused QKV prologue (QK RMSNorm + pa
 V copy, the pass that feeds attention) on the same token count: 161,394 tokens x 56 heads x
 128, rotary width 96. It is bound by HBM and reported in GB/s against 8 TB/s; it is not
 part of ``value``.
+
+An object ``mfma_reference`` times a plain library GEMM (torch.matmul, i.e. hipBLASLt, bf16,
+16384^3) on the same GPU: the dense matrix throughput a tuned library sustains on this chip at
+its power limit, the practical ceiling the attention kernels are compared with
+(``vs_library_gemm``). It is a calibration, not part of ``value``.
 
 roofline.traffic (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
 summary committed under profiles/ for this workload, scaled by the same counters on a copy of
@@ -293,6 +299,35 @@ def cpu_baseline(inp, target_seconds: float = 15.0):
     }
 
 
+def bench_gemm_reference(steps: int = 10, warmup: int = 3, n: int = 16384):
+    """Time torch.matmul (hipBLASLt) on n x n x n bf16; returns the JSON object."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(warmup):
+        torch.matmul(a, b, out=c)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        torch.matmul(a, b, out=c)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    log(f"library GEMM reference: bf16 {n}^3 in {ms:.3f} ms, {tf:.1f} TFLOP/s, "
+        f"{100 * tf / PEAK_BF16_TFLOPS:.1f}% of peak")
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"kernel": f"torch.matmul (hipBLASLt), bf16, {n} x {n} x {n}", "ms": round(ms, 4),
+            "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +342,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward leg")
     ap.add_argument("--fp8-only", action="store_true", help="time only the FP8 forward (for profiling)")
     ap.add_argument("--bwd-only", action="store_true", help="time only the backward (for profiling)")
+    ap.add_argument("--no-gemm-ref", action="store_true", help="skip the library GEMM calibration")
+    ap.add_argument("--gemm-ref-only", action="store_true", help="time only the library GEMM calibration")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward of one rank's share runs on a "
@@ -333,6 +370,9 @@ def main():
         return
     if args.bwd_only:
         print(json.dumps({"attn_bwd": bench_backward(args.config, args.steps, args.warmup)}), flush=True)
+        return
+    if args.gemm_ref_only:
+        print(json.dumps({"mfma_reference": bench_gemm_reference(args.steps, args.warmup)}), flush=True)
         return
 
     t0 = time.perf_counter()
@@ -422,6 +462,10 @@ def main():
         result["attn_bwd"] = bench_backward(args.config, min(max(args.steps, 3), 5), max(min(args.warmup, 2), 1))
     if not args.no_prologue:
         result["qkv_prologue"] = bench_prologue(max(args.steps, 10), max(args.warmup, 2))
+    if not args.no_gemm_ref:
+        ref = bench_gemm_reference()
+        result["mfma_reference"] = ref
+        result["vs_library_gemm"] = round(tflops / ref["tflops"], 4)
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(inp)

@@ -26,6 +26,10 @@
 //  * Copies are 16-byte global -> LDS transfers issued three tiles ahead; the last, partial
 //    tile of a segment is read shifted back to end at the segment end and its re-read rows
 //    are masked (segments shorter than 32 rows repeat their last row instead).
+//  * Each tile is one fixed sequence of MFMAs (24 in dQ, 32 in dK/dV) whose LDS operands are
+//    read two MFMAs ahead, with the vector work placed between them; scheduling barriers hold
+//    the order. The register operands (Q, dO in dQ; K, V in dK/dV) are waited for before the
+//    first tile copy, so no wait inside the loop counts the copies in flight.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -67,20 +71,15 @@ __device__ __forceinline__ void dma4(unsigned voff, const char* base, unsigned l
 __device__ __forceinline__ float lo_f(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_f(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
-// Element v of an accumulator holds row 8 (v / 4) + 4 h32 + v % 4 of its 32-row tile.
-// Rows before `skip` (re-read rows of a shifted last tile) get -inf.
-__device__ __forceinline__ void mask_head(f32x16& S, int skip, int h32) {
-  const int lim = skip - 4 * h32;
+// Element v of an accumulator holds row 8 (v / 4) + 4 h32 + v % 4 of its 32-row tile. Rows
+// outside [lo, hi) get -inf, in place.
+__device__ __forceinline__ void mask_rows(f32x16& S, int lo, int hi, int h32) {
+  const int a = lo - 4 * h32, b = hi - 4 * h32;
 #pragma unroll
-  for (int v = 0; v < 16; ++v)
-    if (8 * (v >> 2) + (v & 3) < lim) S[v] = -INFINITY;
-}
-// Rows at and past `valid` (a single tile shorter than 32 rows) get -inf.
-__device__ __forceinline__ void mask_tail(f32x16& S, int valid, int h32) {
-  const int lim = valid - 4 * h32;
-#pragma unroll
-  for (int v = 0; v < 16; ++v)
-    if (8 * (v >> 2) + (v & 3) >= lim) S[v] = -INFINITY;
+  for (int v = 0; v < 16; ++v) {
+    const int r = 8 * (v >> 2) + (v & 3);
+    S[v] = (r >= a && r < b) ? S[v] : -INFINITY;
+  }
 }
 
 __device__ __forceinline__ void pack_pair(u32x4 (&P)[2], int j, float a, float b) {
@@ -119,6 +118,15 @@ __device__ __forceinline__ Work map_block(const int32_t* cu_seqlens, int n_seqs,
 
 // Copy geometry shared by the streaming kernels: the tile's first row, uniform.
 __device__ __forceinline__ int tile_start(int t, int seg_len) { return min(t * kBT, seg_len - kBT); }
+
+// Masks the rows of the last of n_t tiles that are not this segment's own: a shifted tile
+// repeats its first 32 n_t - seg_len rows from the tile before, a single short tile (a
+// segment under 32 rows) repeats the segment's last row past seg_len.
+__device__ __forceinline__ void mask_last_tile(f32x16& S, int seg_len, int n_t, int h32) {
+  const int lo = seg_len >= kBT ? kBT * n_t - seg_len : 0;
+  const int hi = seg_len >= kBT ? kBT : seg_len;
+  mask_rows(S, lo, hi, h32);
+}
 
 // ---------------------------------------------------------------------------- prep
 
@@ -195,30 +203,55 @@ __device__ __forceinline__ void dq_step(const DqCtx& cx, const DqLane& ln, int t
   wait_vmcnt<kDqOps * (kAhead - 1)>();
   barrier_lds();
   if (n_t > 1) dq_load(cx, t + kAhead);  // a single-tile segment needs no prefetch
-  // S^T first; then the dP^T chain (started at -D) with the exp2 work of P placed between its
-  // MFMAs; dS needs the finished dP^T.
-  f32x16 S = {}, dP = dinit;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) S = mfma(lds_row(ln.raddr[s] + slot), qr[s], S);
+  // One sequence of 24 MFMAs: n = 0..7 S^T (K rows), 8..15 the dP^T chain (V rows, started at
+  // -D) with the exp2 work of P between its MFMAs, 16..23 dQ^T += K^T dS^T (K transposed).
+  // Every LDS operand is read two MFMAs ahead of its use; scheduling barriers hold the order.
+  bf16x8 op[24];
+  auto read = [&](int n) {
+    if (n < 8) op[n] = lds_row(ln.raddr[n] + slot);
+    else if (n < 16) op[n] = lds_row(ln.raddr[n - 8] + slot + kRing);
+    else op[n] = tr_operand(ln.taddr, slot, n - 16);
+  };
+  read(0);
+  read(1);
   sched_fence();
-  if (t == n_t - 1) {
-    if (cx.seg_len >= kBT) mask_head(S, kBT * n_t - cx.seg_len, ln.h32);
-    else mask_tail(S, cx.seg_len, ln.h32);
-  }
+  f32x16 S = {}, dP = dinit;
   float p[16];
+  u32x4 ds[2];
+  bf16x8 dsb[2];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    dP = mfma(lds_row(ln.raddr[s] + slot + kRing), dor[s], dP);
-    p[2 * s] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * s], c, nl));
-    p[2 * s + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * s + 1], c, nl));
+  for (int n = 0; n < 24; ++n) {
+    if (n + 2 < 24) read(n + 2);
+    sched_fence();
+    if (n < 8) {
+      S = mfma(op[n], qr[n], S);
+      if (n == 7 && t == n_t - 1) {
+        sched_fence();
+        mask_last_tile(S, cx.seg_len, n_t, ln.h32);
+      }
+    } else if (n < 16) {
+      const int s = n - 8;
+      dP = mfma(op[n], dor[s], dP);
+      sched_fence();
+      p[2 * s] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * s], c, nl));
+      p[2 * s + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * s + 1], c, nl));
+    } else {
+      const int i = n - 16;
+      if (i == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pack_pair(ds, j, p[2 * j] * dP[2 * j], p[2 * j + 1] * dP[2 * j + 1]);
+        dsb[0] = __builtin_bit_cast(bf16x8, ds[0]);
+      }
+      acc[i & 3] = mfma(op[n], dsb[i >> 2], acc[i & 3]);
+      sched_fence();
+      if (i < 4) {
+        const int j = 4 + i;
+        pack_pair(ds, j, p[2 * j] * dP[2 * j], p[2 * j + 1] * dP[2 * j + 1]);
+        if (i == 3) dsb[1] = __builtin_bit_cast(bf16x8, ds[1]);
+      }
+    }
     sched_fence();
   }
-  u32x4 ds[2];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) pack_pair(ds, j, p[2 * j] * dP[2 * j], p[2 * j + 1] * dP[2 * j + 1]);
-  const bf16x8 dsb[2] = {__builtin_bit_cast(bf16x8, ds[0]), __builtin_bit_cast(bf16x8, ds[1])};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i & 3] = mfma(tr_operand(ln.taddr, slot, i), dsb[i >> 2], acc[i & 3]);
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -266,6 +299,9 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       dor[s] = *(const bf16x8*)(dout + off + 16 * s);
     }
   }
+  // As in the dK/dV kernel: wait for these before any tile copy is issued.
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(qr[s]), "v"(dor[s]));
   const float nl = c * ws_nl[(int64_t)w.head * total_tokens + tok];  // -LSE log2(e)
   f32x16 dinit;  // -D in every element: the starting value of each tile's dP^T
   {
@@ -360,11 +396,12 @@ __device__ __forceinline__ void kv_load_short(const KvCtx& cx, int lane, int wav
 
 struct KvLane {
   int lane, h32, l32;
-  unsigned raddr[8];  // row-layout read address of 16-dim step s (region 0, slot 0)
-  unsigned qtaddr;    // transposed-read lane base, region 2 (Q)
-  unsigned dotaddr;   // transposed-read lane base, region 3 (dO)
+  unsigned raddr0;    // row-layout read address of 16-dim step 0 (region 0, slot 0); step s is
+                      // raddr0 ^ (s << 5): the step only flips chunk bits 1..3 of the swizzle
+  unsigned qtaddr;    // transposed-read lane base, region 2 (Q); region 3 (dO) is + kRing
   unsigned staddr;    // this lane's stats: float 8 a + 4 h32 of the tile, a = 0..3 (slot 0)
 };
+
 
 template <int U>
 __device__ __forceinline__ void kv_step(const KvCtx& cx, const KvLane& ln, int t, int n_t, const bf16x8 (&kr)[8],
@@ -376,47 +413,72 @@ __device__ __forceinline__ void kv_step(const KvCtx& cx, const KvLane& ln, int t
   if (n_t > 1) kv_load(cx, t + kAhead, ln.lane);  // a single-tile segment needs no prefetch
   // S = Q K^T - LSE / scale and dP = dO V^T - D: lane = key l32, element v = query
   // 8 (v / 4) + 4 h32 + v % 4, whose stats are the 4 consecutive floats at 8 (v / 4) + 4 h32.
+  // One sequence of 32 MFMAs: n = 0..7 S (Q rows), 8..15 dP (dO rows) with P's exp2 work,
+  // 16..23 dV^T += dO^T P with dS's work, 24..31 dK^T += Q^T dS. Every LDS operand is read
+  // two MFMAs ahead of its use; scheduling barriers hold the order.
+  bf16x8 op[32];
+  // The row-read base is made opaque per step and again before the dO rows, so the compiler
+  // forms each step's address where it is read rather than keeping eight of them live.
+  unsigned r0 = ln.raddr0;
+  asm volatile("" : "+v"(r0));
+  auto read = [&](int n) {
+    if (n < 8) op[n] = lds_row((r0 ^ (n << 5)) + slot);
+    else if (n < 16) op[n] = lds_row((r0 ^ ((n - 8) << 5)) + slot + kRing);
+    else if (n < 24) op[n] = tr_operand(ln.qtaddr, slot + kRing, n - 16);
+    else op[n] = tr_operand(ln.qtaddr, slot, n - 24);
+  };
   f32x16 S, dP;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const f32x4 ls = *(lds_f32x4*)(uintptr_t)(ln.staddr + sslot + 32 * a);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) S[4 * a + b] = ls[b];
+  }
+  read(0);
+  read(1);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
     const f32x4 nd = *(lds_f32x4*)(uintptr_t)(ln.staddr + sslot + 32 * a + kBT * 4);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      S[4 * a + b] = ls[b];
-      dP[4 * a + b] = nd[b];
-    }
+    for (int b = 0; b < 4; ++b) dP[4 * a + b] = nd[b];
   }
-  // S first; then the dP chain with P's exp2 work placed between its MFMAs; then dV with
-  // dS's work between its MFMAs; then dK. Scheduling barriers hold this order, so each
-  // wave keeps the matrix pipe fed while its vector ALU works.
-#pragma unroll
-  for (int s = 0; s < 8; ++s) S = mfma(lds_row(ln.raddr[s] + slot), kr[s], S);
   sched_fence();
-  if (t == n_t - 1) {
-    if (cx.seg_len >= kBT) mask_head(S, kBT * n_t - cx.seg_len, ln.h32);
-    else mask_tail(S, cx.seg_len, ln.h32);
-  }
   // P and dS are formed in place of S and dP (fewer live registers).
   u32x4 pb[2], sb[2];
+  bf16x8 P[2], dS[2];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    dP = mfma(lds_row(ln.raddr[s] + slot + kRing), vr[s], dP);
-    S[2 * s] = __builtin_amdgcn_exp2f(S[2 * s] * c);
-    S[2 * s + 1] = __builtin_amdgcn_exp2f(S[2 * s + 1] * c);
-    pack_pair(pb, s, S[2 * s], S[2 * s + 1]);
+  for (int n = 0; n < 32; ++n) {
+    if (n == 6) asm volatile("" : "+v"(r0));
+    if (n + 2 < 32) read(n + 2);
+    sched_fence();
+    if (n < 8) {
+      S = mfma(op[n], kr[n], S);
+      if (n == 7 && t == n_t - 1) {
+        sched_fence();
+        mask_last_tile(S, cx.seg_len, n_t, ln.h32);
+      }
+    } else if (n < 16) {
+      const int s = n - 8;
+      dP = mfma(op[n], vr[s], dP);
+      sched_fence();
+      S[2 * s] = __builtin_amdgcn_exp2f(S[2 * s] * c);
+      S[2 * s + 1] = __builtin_amdgcn_exp2f(S[2 * s + 1] * c);
+      pack_pair(pb, s, S[2 * s], S[2 * s + 1]);
+      if (s == 3) P[0] = __builtin_bit_cast(bf16x8, pb[0]);
+      if (s == 7) P[1] = __builtin_bit_cast(bf16x8, pb[1]);
+    } else if (n < 24) {
+      const int i = n - 16;
+      dv[i & 3] = mfma(op[n], P[i >> 2], dv[i & 3]);
+      sched_fence();
+      pack_pair(sb, i, S[2 * i] * dP[2 * i], S[2 * i + 1] * dP[2 * i + 1]);
+      if (i == 3) dS[0] = __builtin_bit_cast(bf16x8, sb[0]);
+      if (i == 7) dS[1] = __builtin_bit_cast(bf16x8, sb[1]);
+    } else {
+      const int i = n - 24;
+      dk[i & 3] = mfma(op[n], dS[i >> 2], dk[i & 3]);
+    }
     sched_fence();
   }
-  const bf16x8 P[2] = {__builtin_bit_cast(bf16x8, pb[0]), __builtin_bit_cast(bf16x8, pb[1])};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    dv[i & 3] = mfma(tr_operand(ln.dotaddr, slot, i), P[i >> 2], dv[i & 3]);
-    pack_pair(sb, i, S[2 * i] * dP[2 * i], S[2 * i + 1] * dP[2 * i + 1]);
-    sched_fence();
-  }
-  const bf16x8 dS[2] = {__builtin_bit_cast(bf16x8, sb[0]), __builtin_bit_cast(bf16x8, sb[1])};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dk[i & 3] = mfma(tr_operand(ln.qtaddr, slot, i), dS[i >> 2], dk[i & 3]);
 }
 
 __device__ __forceinline__ void store_rows_t(uint16_t* orow, const f32x16 (&acc)[4], float mul, int h32) {
@@ -470,10 +532,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   ln.lane = lane;
   ln.h32 = lane >> 5;
   ln.l32 = lane & 31;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) ln.raddr[s] = row_read_addr(lds_base, ln.l32, ln.h32, s);
+  ln.raddr0 = row_read_addr(lds_base, ln.l32, ln.h32, 0);
   ln.qtaddr = tr_read_base(lds_base + 2 * kRing, lane);
-  ln.dotaddr = tr_read_base(lds_base + 3 * kRing, lane);
   ln.staddr = lds_base + 4 * kRing + 4 * (4 * ln.h32);
 
   // This lane's key: K and V as B operands (k[key][16 s + 8 h32 .. +7]).
@@ -490,6 +550,11 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       vr[s] = *(const bf16x8*)(v + off + 16 * s);
     }
   }
+  // Wait for K and V here, before any tile copy is issued. Left to the compiler, that wait
+  // sat at their first use inside the tile loop, where it also counted the copies of the
+  // tiles ahead and so drained the prefetch on every tile.
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(kr[s]), "v"(vr[s]));
   f32x16 dka[4], dva[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {

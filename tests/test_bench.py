@@ -46,3 +46,6 @@ def test_bench_json_line(gpu):
         assert key in roof, key
     assert roof["bound"] == "mfma" and roof["peak"] == 2500.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    ref = line["mfma_reference"]  # the library GEMM calibration
+    assert 0 < ref["tflops"] < 2500.0 and abs(ref["frac_of_peak"] - ref["tflops"] / 2500.0) < 1e-3
+    assert abs(line["vs_library_gemm"] - line["value"] / ref["tflops"]) < 1e-3
