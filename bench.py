@@ -25,8 +25,8 @@ V copy, the pass that feeds attention) on the same token count: 161,394 tokens x
 part of ``value``.
 
 An object ``mfma_reference`` times a plain library GEMM (torch.matmul, i.e. hipBLASLt, bf16,
-16384^3) on the same GPU: the dense matrix throughput a tuned library sustains on this chip at
-its power limit, the practical ceiling the attention kernels are compared with
+16384^3, 50 calls back to back) on the same GPU: the dense matrix throughput a tuned library
+sustains on this chip at its power limit, the practical ceiling the attention kernels are compared with
 (``vs_library_gemm``). It is a calibration, not part of ``value``.
 
 roofline.traffic (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
@@ -299,8 +299,9 @@ def cpu_baseline(inp, target_seconds: float = 15.0):
     }
 
 
-def bench_gemm_reference(steps: int = 10, warmup: int = 3, n: int = 16384):
-    """Time torch.matmul (hipBLASLt) on n x n x n bf16; returns the JSON object."""
+def bench_gemm_reference(steps: int = 50, warmup: int = 5, n: int = 16384):
+    """Time torch.matmul (hipBLASLt) on n x n x n bf16; returns the JSON object. The default 50 calls
+    (about a third of a second) run as long as one attention step, so both meet the same power limit."""
     import torch
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
@@ -372,7 +373,7 @@ def main():
         print(json.dumps({"attn_bwd": bench_backward(args.config, args.steps, args.warmup)}), flush=True)
         return
     if args.gemm_ref_only:
-        print(json.dumps({"mfma_reference": bench_gemm_reference(args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"mfma_reference": bench_gemm_reference(max(args.steps, 10), args.warmup)}), flush=True)
         return
 
     t0 = time.perf_counter()
