@@ -27,7 +27,8 @@ part of ``value``.
 An object ``mfma_reference`` times a plain library GEMM (torch.matmul, i.e. hipBLASLt, bf16,
 16384^3, 50 calls back to back) on the same GPU: the dense matrix throughput a tuned library
 sustains on this chip at its power limit, the practical ceiling the attention kernels are compared with
-(``vs_library_gemm``). It is a calibration, not part of ``value``.
+(``vs_library_gemm``). ``attn_fwd_fp8`` carries the same for e4m3 (torch._scaled_mm). They are
+calibrations, not part of ``value``.
 
 roofline.traffic (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
 summary committed under profiles/ for this workload, scaled by the same counters on a copy of
@@ -299,9 +300,10 @@ def cpu_baseline(inp, target_seconds: float = 15.0):
     }
 
 
-def bench_gemm_reference(steps: int = 50, warmup: int = 5, n: int = 16384):
-    """Time torch.matmul (hipBLASLt) on n x n x n bf16; returns the JSON object. The default 50 calls
-    (about a third of a second) run as long as one attention step, so both meet the same power limit."""
+def bench_gemm_reference(dtype: str = "bf16", steps: int = 50, warmup: int = 5, n: int = 16384):
+    """Time a library GEMM on n x n x n: torch.matmul (hipBLASLt) for ``bf16``, torch._scaled_mm
+    (hipBLASLt, e4m3 inputs, unit scales, bf16 output) for ``fp8``; returns the JSON object. The
+    default calls run about as long as one attention step, so both meet the same power limit."""
     import torch
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
@@ -309,24 +311,37 @@ def bench_gemm_reference(steps: int = 50, warmup: int = 5, n: int = 16384):
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
     c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    if dtype == "bf16":
+        def call():
+            torch.matmul(a, b, out=c)
+        name, peak = f"torch.matmul (hipBLASLt), bf16, {n} x {n} x {n}", PEAK_BF16_TFLOPS
+    elif dtype == "fp8":
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+        b8t = b8.t()  # the column-major second operand _scaled_mm takes
+        one = torch.ones((), device=dev, dtype=torch.float32)
+
+        def call():
+            torch._scaled_mm(a8, b8t, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        name, peak = f"torch._scaled_mm (hipBLASLt), e4m3 in, bf16 out, {n} x {n} x {n}", PEAK_FP8_TFLOPS
+    else:
+        raise ValueError(dtype)
     for _ in range(warmup):
-        torch.matmul(a, b, out=c)
+        call()
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     e0.record(stream)
     for _ in range(steps):
-        torch.matmul(a, b, out=c)
+        call()
     e1.record(stream)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
     tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-    log(f"library GEMM reference: bf16 {n}^3 in {ms:.3f} ms, {tf:.1f} TFLOP/s, "
-        f"{100 * tf / PEAK_BF16_TFLOPS:.1f}% of peak")
+    log(f"library GEMM reference: {dtype} {n}^3 in {ms:.3f} ms, {tf:.1f} TFLOP/s, {100 * tf / peak:.1f}% of peak")
     del a, b, c
     torch.cuda.empty_cache()
-    return {"kernel": f"torch.matmul (hipBLASLt), bf16, {n} x {n} x {n}", "ms": round(ms, 4),
-            "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "steps": steps}
+    return {"kernel": name, "ms": round(ms, 4), "tflops": round(tf, 2), "frac_of_peak": round(tf / peak, 4),
+            "steps": steps}
 
 
 def main():
@@ -373,7 +388,9 @@ def main():
         print(json.dumps({"attn_bwd": bench_backward(args.config, args.steps, args.warmup)}), flush=True)
         return
     if args.gemm_ref_only:
-        print(json.dumps({"mfma_reference": bench_gemm_reference(max(args.steps, 10), args.warmup)}), flush=True)
+        print(json.dumps({"mfma_reference": bench_gemm_reference("bf16", max(args.steps, 10), args.warmup),
+                          "mfma_reference_fp8": bench_gemm_reference("fp8", max(args.steps, 10), args.warmup)}),
+              flush=True)
         return
 
     t0 = time.perf_counter()
@@ -459,12 +476,17 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_fp8:
         result["attn_fwd_fp8"] = bench_fp8(args.config, min(max(args.steps, 3), 10), max(min(args.warmup, 2), 1))
+        if not args.no_gemm_ref:
+            ref8 = bench_gemm_reference("fp8", steps=64)
+            result["attn_fwd_fp8"]["mfma_reference"] = ref8
+            result["attn_fwd_fp8"]["vs_library_gemm"] = round(result["attn_fwd_fp8"]["roofline"]["achieved"] /
+                                                              ref8["tflops"], 4)
     if not args.no_bwd:
         result["attn_bwd"] = bench_backward(args.config, min(max(args.steps, 3), 5), max(min(args.warmup, 2), 1))
     if not args.no_prologue:
         result["qkv_prologue"] = bench_prologue(max(args.steps, 10), max(args.warmup, 2))
     if not args.no_gemm_ref:
-        ref = bench_gemm_reference()
+        ref = bench_gemm_reference("bf16")
         result["mfma_reference"] = ref
         result["vs_library_gemm"] = round(tflops / ref["tflops"], 4)
     if not args.no_cpu_baseline:
