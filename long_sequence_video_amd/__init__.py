@@ -1,12 +1,15 @@
-"""lsv: dense non-causal varlen BF16 attention forward for MI355X (gfx950), and the fused
-QKV prologue (QK RMSNorm + partial RoPE) that feeds it.
+"""lsv: dense non-causal varlen attention for MI355X (gfx950): the BF16 forward, its
+deterministic backward, an FP8 (e4m3) forward, and the fused QKV prologue (QK RMSNorm +
+partial RoPE) that feeds them.
 
 Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in-tree by
 ``python -m long_sequence_video_amd.build``). The functions named like the C entry points
-(``lsv_attn_fwd``, ``lsv_qkv_prologue``, ``lsv_status_string``, ``lsv_device_peak``,
-``lsv_tile_config``) only marshal arguments; ``attn_fwd`` and ``qkv_prologue`` add
-torch-tensor conveniences (output allocation, the current stream). There is no fallback:
-if the library is missing or a call fails, an exception is raised.
+(``lsv_attn_fwd``, ``lsv_attn_fwd_fp8``, ``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``,
+``lsv_qkv_prologue``, ``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only
+marshal arguments; ``attn_fwd``, ``attn_fwd_fp8``, ``attn_bwd`` and ``qkv_prologue`` add
+torch-tensor conveniences (shape checks, output and workspace allocation, the current
+stream). There is no fallback: if the library is missing or a call fails, an exception is
+raised.
 """
 
 from __future__ import annotations
@@ -176,6 +179,8 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | 
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
     if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
+    if out.device != dev or lse.device != dev:
+        raise ValueError("out and lse must be on the same GPU as q")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         rc = lsv_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -335,6 +340,8 @@ def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: floa
         raise ValueError("out must be a contiguous bfloat16 [total_tokens, heads, head_dim] tensor")
     if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
+    if out.device != dev or lse.device != dev:
+        raise ValueError("out and lse must be on the same GPU as q8")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         rc = lsv_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), descale_q, descale_k, descale_v,

@@ -141,6 +141,28 @@ def test_unsupported_head_dim_raises(gpu):
     assert list(out.shape) == [7, 2, 128] and list(lse.shape) == [2, 7]
 
 
+def test_outputs_on_another_device_are_rejected(gpu):
+    """Preallocated outputs must live on the inputs' GPU: a host tensor would hand the kernel a
+    host address. The binding refuses before any launch, and the outputs stay untouched."""
+    import torch
+    import long_sequence_video_amd as lsv
+    q = torch.zeros((40, 2, 128), dtype=torch.bfloat16, device=gpu)
+    cu = torch.tensor([0, 40], dtype=torch.int32, device=gpu)
+    out_host = torch.full((40, 2, 128), 3.0, dtype=torch.bfloat16)
+    lse_host = torch.full((2, 40), 3.0, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        lsv.attn_fwd(q, q, q, cu, 40, 0.125, out=out_host)
+    with pytest.raises(ValueError):
+        lsv.attn_fwd(q, q, q, cu, 40, 0.125, lse=lse_host)
+    q8 = torch.zeros((40, 2, 128), dtype=torch.uint8, device=gpu)
+    with pytest.raises(ValueError):
+        lsv.attn_fwd_fp8(q8, q8, q8, 1.0, 1.0, 1.0, cu, 40, 0.125, out=out_host)
+    with pytest.raises(ValueError):
+        lsv.attn_fwd_fp8(q8, q8, q8, 1.0, 1.0, 1.0, cu, 40, 0.125, lse=lse_host)
+    torch.cuda.synchronize(gpu)
+    assert bool((out_host == 3.0).all()) and bool((lse_host == 3.0).all())
+
+
 # ---------------------------------------------------------------- closed forms on the GPU
 
 def test_dominant_logit_gives_exact_value_row(gpu):
