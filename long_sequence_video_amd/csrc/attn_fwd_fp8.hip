@@ -21,7 +21,8 @@
 //    (no fp8 dot instruction on gfx950). The LSE uses the fp32 sum of the unquantised weights.
 //  * Software pipeline per key tile t: one sequence of nine MFMAs, S(t+1) = Q K(t+1)^T, then
 //    O += P(t-1) V(t-1) and the weight sum of P(t-1), with the exp2 / e4m3 work of S(t) placed
-//    between them (scheduling barriers hold the order).
+//    between them (scheduling barriers hold the order). The running max is checked after the
+//    tile, and only when this lane's weights of the tile sum past what a raise requires.
 //  * Softmax: p = exp2(s c - m c + 5) with c = scale dq dk log2(e) and m a running row max
 //    raised only when a tile exceeds it by more than 3 log2 units (then O and the sums are
 //    rescaled, O after the tile's MFMAs): weights stay in [0, 2^8], below e4m3's 448 (its
@@ -31,7 +32,8 @@
 //    later key exceeds the first tile by 3.8 log2 units, which long rows do routinely.
 //  * LDS: K and V rows of 128 bytes with 16-byte chunk c of row r stored at c ^ sw8(r), a
 //    permutation of the row-pair index that keeps the row reads and the transposed reads free
-//    of bank conflicts. K and V stream through an 8-slot ring, 4 tiles ahead, one barrier per tile.
+//    of bank conflicts. K and V stream through an 8-slot ring, 5 tiles ahead, one barrier per two
+//    tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -56,14 +58,23 @@ constexpr int kBK = 64;                   // keys per tile
 constexpr int kRow8 = kD;                 // bytes per fp8 row
 constexpr int kSlot = kBK * kRow8;        // 8 KB per tile
 constexpr int kSlots = 8;
-constexpr int kAhead = 4;
+constexpr int kAhead = 5;
 constexpr int kRingBytes = kSlots * kSlot;
 constexpr int kLdsBytes = 2 * kRingBytes;
 constexpr int kOpsPerTile = 2;            // one 1 KB copy of K and one of V per wave per tile
 constexpr float kRefLog2 = 5.0f;          // the reference weight: 2^5
 constexpr float kLazyLog2 = 3.0f;         // raise the running max only beyond this (log2 units)
+// A weight above 2^(kRefLog2 + kLazyLog2) = 256 puts its lane's tile sum above this (a sum of
+// non-negative terms is at least its largest term, up to fp32 rounding of ~2^-19 relative).
+constexpr float kCheckSum = 255.0f;
+static_assert(kRefLog2 + kLazyLog2 == 8.0f, "kCheckSum assumes a raise threshold of 2^8");
 constexpr unsigned kOnes = 0x38383838u;   // four e4m3 ones
-static_assert(kAhead >= 2 && kAhead <= kSlots - 2, "ring too small for the prefetch distance");
+// The workgroup synchronises after odd tiles only. Between two barriers a wave runs at most
+// tiles t+1, t+2 (t odd) and copies tiles t+1+kAhead, t+2+kAhead; a wave still behind has
+// finished tile t, so it may read V(t), K(t+2) (tile t+1) or V(t+1), K(t+3) (tile t+2): the
+// written slots must be none of tiles t .. t+3, i.e. kAhead <= kSlots - 3. Each barrier
+// follows the wait for tile t+3 (read as K by tile t+2), leaving kAhead - 3 tiles in flight.
+static_assert(kAhead >= 3 && kAhead <= kSlots - 3, "ring too small for the prefetch distance");
 
 // Chunk swizzle of a row: with k = (row / 2) % 8 (rows 2k and 2k + 1 sit in the two halves of
 // the 64 banks), 4 (k % 2) + k / 2. Any 8 even (or odd) rows of a 16-row block get 8 distinct
@@ -248,27 +259,16 @@ __device__ __forceinline__ void scale_o(Acc& acc, float r) {
 __device__ __forceinline__ unsigned slot_of(int t) { return (unsigned)(t & (kSlots - 1)) * kSlot; }
 
 // Steady-state key tile t (1 <= t <= n_kt - 2). On entry S(t) and P(t-1) are complete and
-// tile t+1 is in LDS. First the lazy max check of S(t): if some row of the wave exceeds its
-// max by more than the margin (rare), the max is raised and l rescaled at once, and O and
-// the weight sums after this tile's MFMAs (which still add P(t-1) V(t-1), weighted against
-// the old max). Then one sequence of nine MFMAs, S(t+1) = Q K(t+1)^T (four, first, so that
-// the next tile's max check finds them done), O += P(t-1) V(t-1) (four), the weight sum of
-// P(t-1), with the weights P(t) of S(t) computed between them, operands read one MFMA
-// ahead and the copy of tile t + kAhead issued after the fifth.
-// Then tile t+2 is waited for and the workgroup synchronises.
+// tile t+1 is in LDS. One sequence of nine MFMAs, S(t+1) = Q K(t+1)^T (four, first), O +=
+// P(t-1) V(t-1) (four) and the weight sum of P(t-1), with the weights P(t) of S(t), against the
+// running max, computed between them, operands read one MFMA ahead and the copy of tile
+// t + kAhead issued after the fifth. Then the lazy max check of S(t), gated so that the row max
+// is computed only when a raise is possible (rare); a raise rescales l, O and the weight sums
+// and redoes P(t). After an odd tile, tile t+3 is waited for and the workgroup synchronises.
 template <int U>
 __device__ __forceinline__ void step(const Ctx& cx, int t, Acc& acc, const f32x16 (&Scur)[2], f32x16 (&Snext)[2],
                                      const i32x8& Pprev, i32x8& Pcur, const i32x8 (&qr)[2], const Lane& ln,
                                      const i32x8& sel) {
-  const float mx = row_max(Scur);
-  const bool raise = __builtin_amdgcn_ballot_w64(mx > acc.m + cx.lazy) != 0;  // wave-uniform
-  float r = 1.f;
-  if (raise) {
-    const float mnew = fmaxf(acc.m, mx);
-    r = __builtin_amdgcn_exp2f((acc.m - mnew) * cx.c);
-    acc.l *= r;
-    acc.m = mnew;
-  }
   const float nr = kRefLog2 - acc.m * cx.c;
   // t % kSlots == U: both ring slots are compile-time offsets (LDS read immediates).
   const Bases b = bases(ln, ((U + 1) % kSlots) * kSlot, ((U + kSlots - 1) % kSlots) * kSlot);
@@ -280,6 +280,7 @@ __device__ __forceinline__ void step(const Ctx& cx, int t, Acc& acc, const f32x1
   read(0);
   sched_fence();
   f32x16 s = {};
+  float ls = 0.f;  // this tile's weights, this lane's 32 keys
 #pragma unroll
   for (int n = 0; n < 9; ++n) {
     if (n < 4) {
@@ -293,14 +294,32 @@ __device__ __forceinline__ void step(const Ctx& cx, int t, Acc& acc, const f32x1
     }
     if (n + 1 < 9) read(n + 1);
     if (n == 4) load_tile(cx, t + kAhead);
-    if (n < 8) softmax_dword(Scur, Pcur, acc.l, cx.c, nr, n);
+    if (n < 8) softmax_dword(Scur, Pcur, ls, cx.c, nr, n);
     sched_fence();
   }
-  // P(t) and the sum must be complete here (they must not sink into the next tile).
-  asm volatile("" : "+v"(Pcur), "+v"(acc.l));
-  if (raise) scale_o(acc, r);
-  wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
-  barrier_lds();
+  // P(t) and its sum must be complete here (they must not sink into the next tile).
+  asm volatile("" : "+v"(Pcur), "+v"(ls));
+  // The lazy max check, gated: a raise needs a score above m + lazy, i.e. a weight above
+  // 2^(kRefLog2 + kLazyLog2), and so this lane's tile sum above kCheckSum. Only then (rare) is
+  // the row max computed; on a raise, l, O and the weight sums are rescaled (O after this
+  // tile's MFMAs, which still add P(t-1) weighted against the old max) and P(t) is redone.
+  if (__builtin_amdgcn_ballot_w64(ls > kCheckSum) != 0) {
+    const float mx = row_max(Scur);
+    if (__builtin_amdgcn_ballot_w64(mx > acc.m + cx.lazy) != 0) {  // wave-uniform
+      const float mnew = fmaxf(acc.m, mx);
+      const float r = __builtin_amdgcn_exp2f((acc.m - mnew) * cx.c);
+      acc.l *= r;
+      acc.m = mnew;
+      ls = 0.f;
+      softmax_all(Scur, Pcur, ls, cx.c, kRefLog2 - mnew * cx.c);
+      scale_o(acc, r);
+    }
+  }
+  acc.l += ls;
+  if (U & 1) {
+    wait_vmcnt<kOpsPerTile * (kAhead - 3)>();
+    barrier_lds();
+  }
 }
 
 // The last tile tl = n_kt - 1 >= 1 (loaded shifted to end at the segment end): P(tl-1) V(tl-1),
@@ -357,7 +376,7 @@ __device__ __forceinline__ void run(const Ctx& cx, int n_kt, Acc& acc, const i32
   softmax_all(SA, PA, acc.l, cx.c, kRefLog2 - acc.m * cx.c);
   qk_tile(bases(ln, slot_of(1), 0), qr, SB);
   load_tile(cx, kAhead);
-  wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
+  wait_vmcnt<kOpsPerTile * (kAhead - 3)>();  // as after an odd tile: tiles 2 and 3 are read next
   barrier_lds();
 
   const int last = n_kt - 2;
