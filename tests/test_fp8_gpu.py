@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from long_sequence_video_amd import inputs as gen
-from oracle import attention_fp8_fp64, bf16_bits_to_f64
+from oracle import attention_fp8_fp64, bf16_bits_to_f64, e4m3_bits_to_f64
 from tests.gpu_common import from_dev, say
 
 pytestmark = pytest.mark.gpu
@@ -132,6 +132,23 @@ def test_fp8_dominant_late_key(gpu):
     say("case fp8 dominant key")
     out, lse = run_fp8(f8, gpu)
     compare_fp8(f8, out, lse, label="fp8 dominant")
+
+
+def test_fp8_identical_keys_check_without_raise(gpu):
+    """Identical keys give every key of a row the reference weight 2^5, so each lane's tile sum
+    is 32 x 32 = 1024 and passes the gate of the lazy max check on every tile; the row max then
+    equals the running max and no raise follows. O is the mean of the segment's V rows."""
+    inp = gen.generate([700, 129], 2, seed=55, name="fp8_same_keys")
+    f8 = gen.quantize_fp8(inp)
+    for a, b in zip(f8.cu_seqlens[:-1], f8.cu_seqlens[1:]):
+        f8.k[a:b] = f8.k[a]
+    say("case fp8 identical keys")
+    out, lse = run_fp8(f8, gpu)
+    compare_fp8(f8, out, lse, label="fp8 identical keys")
+    for a, b in zip(f8.cu_seqlens[:-1], f8.cu_seqlens[1:]):
+        mean_v = f8.descale_v * e4m3_bits_to_f64(f8.v[a:b]).mean(axis=0)
+        got = bf16_bits_to_f64(out[a:b])
+        assert np.abs(got - mean_v[None]).max() <= 2e-2, (a, b)
 
 
 def _sampled(f8, n, seed, edge=128):
