@@ -360,6 +360,9 @@ def main():
     ap.add_argument("--bwd-only", action="store_true", help="time only the backward (for profiling)")
     ap.add_argument("--no-gemm-ref", action="store_true", help="skip the library GEMM calibration")
     ap.add_argument("--gemm-ref-only", action="store_true", help="time only the library GEMM calibration")
+    ap.add_argument("--split", default="auto",
+                    help="key ranges per segment for the forward (lsv_attn_fwd_split): a number, or 'auto' "
+                         "(choose_split: 1 unless the launch leaves the last round of compute units mostly idle)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward of one rank's share runs on a "
@@ -403,9 +406,18 @@ def main():
     lse = torch.empty((inp.n_heads, inp.total_tokens), dtype=torch.float32, device=dev)
     flops = inp.flops()
     ms = inp.max_seqlen
+    n_split = lsv.choose_split(inp.seqlens, inp.n_heads) if args.split == "auto" else int(args.split)
+    ws = None
+    if n_split > 1:
+        ws = torch.empty(lsv.lsv_attn_fwd_split_workspace_size(inp.total_tokens, inp.n_heads, n_split),
+                         dtype=torch.uint8, device=dev)
+        log(f"forward with {n_split} key ranges per segment (lsv_attn_fwd_split)")
 
     def step():
-        lsv.attn_fwd(q, k, v, cu, ms, inp.scale, out=out, lse=lse)
+        if n_split == 1:
+            lsv.attn_fwd(q, k, v, cu, ms, inp.scale, out=out, lse=lse)
+        else:
+            lsv.attn_fwd_split(q, k, v, cu, ms, inp.scale, n_split, out=out, lse=lse, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -426,7 +438,10 @@ def main():
     log(f"{args.config}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s, {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
 
     peak_at_clock, cus, khz = lsv.lsv_device_peak(0)
-    traffic, traffic_src = measured_traffic(inp.name)
+    if n_split == 1:
+        traffic, traffic_src = measured_traffic(inp.name)
+    else:
+        traffic, traffic_src = None, "not measured for the key-split launch"
     # HBM-minimal bytes per launch: q, k, v read once, O written once (bf16), LSE (fp32).
     algorithmic_bytes = 4 * inp.total_tokens * inp.n_heads * inp.head_dim * 2 + inp.total_tokens * inp.n_heads * 4
     result = {
@@ -451,6 +466,7 @@ def main():
             "causal": False,
             "flops_per_step": flops,
             "parallelism": "single GPU",
+            "key_split": n_split,
         },
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms": {"p50": round(float(np.percentile(per_step, 50)), 4),
@@ -466,13 +482,13 @@ def main():
             "traffic_unit": "HBM bytes per launch",
             "traffic_source": traffic_src,
             "algorithmic_hbm_bytes": algorithmic_bytes,
-            "kernel": "attn_fwd_kernel",
+            "kernel": "attn_fwd_kernel" if n_split == 1 else "attn_fwd_split_kernel + attn_fwd_combine_kernel",
             "peak_at_reported_clock": round(peak_at_clock, 1),
             "compute_units": cus,
             "clock_mhz": khz // 1000,
         },
     }
-    del q, k, v, out, lse
+    del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
     if not args.no_fp8:
         result["attn_fwd_fp8"] = bench_fp8(args.config, min(max(args.steps, 3), 10), max(min(args.warmup, 2), 1))

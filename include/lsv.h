@@ -65,6 +65,32 @@ int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
                  float scale, void* stream);
 
+/* Workspace bytes lsv_attn_fwd_split needs for n_split key ranges: n_split partial rows of
+ * head_dim + 1 fp32 values per (token, head), i.e. 4 * n_split * total_tokens * n_heads * 129;
+ * 0 for n_split = 1. Returns -1 for a negative size, n_heads < 1 or n_split outside [1, 8]. */
+int64_t lsv_attn_fwd_split_workspace_size(int64_t total_tokens, int32_t n_heads, int32_t n_split);
+
+/* Attention forward with each segment's keys cut into n_split consecutive ranges
+ * (asynchronous, two kernels on the caller's stream). The same operation as lsv_attn_fwd (the
+ * varlen forward of FastVideo #2049), computed the way split-K attention combines partial
+ * softmaxes: each (query tile, range) workgroup writes its range's normalised fp32 O_r and
+ * LSE_r into the workspace, and a second pass writes, per row,
+ *     LSE = ln sum_r exp(LSE_r),   O = sum_r exp(LSE_r - LSE) O_r   (bf16, nearest even)
+ * over the non-empty ranges. A range holds ceil(ceil(len / n_split) / 32) * 32 keys, the last
+ * one the rest. More, shorter workgroups fill the last round of 256 compute units better when
+ * a launch has few query tiles (e.g. 14 heads x 19,394 tokens: 1,064 workgroups); the result
+ * differs from lsv_attn_fwd's by rounding only, and is deterministic.
+ *
+ * q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+ * stream: as for lsv_attn_fwd (same layouts, limits and skipped-segment rule).
+ * n_split      1 to 8; 1 is lsv_attn_fwd itself (the workspace is not used).
+ * workspace    device pointer, 16-byte aligned, at least lsv_attn_fwd_split_workspace_size
+ *              bytes (else LSV_ERR_INVALID_ARG); overwritten. Owned by the caller.
+ */
+int lsv_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                       int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                       float scale, int32_t n_split, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* FP8 (e4m3) attention forward on the caller's stream (asynchronous).
  *
  * The operation (TensorRT-LLM PR #21275, the MiniMax-H3 recipe commit: attention with

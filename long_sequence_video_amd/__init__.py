@@ -4,9 +4,10 @@ partial RoPE) that feeds them.
 
 Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in-tree by
 ``python -m long_sequence_video_amd.build``). The functions named like the C entry points
-(``lsv_attn_fwd``, ``lsv_attn_fwd_fp8``, ``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``,
+(``lsv_attn_fwd``, ``lsv_attn_fwd_split``, ``lsv_attn_fwd_split_workspace_size``, ``lsv_attn_fwd_fp8``,
+``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``,
 ``lsv_qkv_prologue``, ``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only
-marshal arguments; ``attn_fwd``, ``attn_fwd_fp8``, ``attn_bwd`` and ``qkv_prologue`` add
+marshal arguments; ``attn_fwd``, ``attn_fwd_split``, ``attn_fwd_fp8``, ``attn_bwd`` and ``qkv_prologue`` add
 torch-tensor conveniences (shape checks, output and workspace allocation, the current
 stream). There is no fallback: if the library is missing or a call fails, an exception is
 raised.
@@ -19,14 +20,16 @@ import math
 import os
 
 __all__ = [
-    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_attn_fwd_fp8", "attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size",
-    "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak", "lsv_tile_config", "attn_fwd", "attn_bwd",
-    "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
+    "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_workspace_size",
+    "lsv_attn_fwd_fp8", "attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue",
+    "lsv_status_string", "lsv_device_peak", "lsv_tile_config", "attn_fwd", "attn_fwd_split", "choose_split",
+    "attn_bwd", "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
-EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue",
-                    "lsv_status_string", "lsv_device_peak", "lsv_tile_config")
+EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_workspace_size", "lsv_attn_fwd_fp8",
+                    "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue", "lsv_status_string",
+                    "lsv_device_peak", "lsv_tile_config")
 
 LSV_OK = 0
 LSV_ERR_INVALID_ARG = -1
@@ -57,6 +60,11 @@ def load_library(path: str = LIB_PATH):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.lsv_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, vp]
     lib.lsv_attn_fwd.restype = ctypes.c_int
+    lib.lsv_attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, i32, vp, i64,
+                                       vp]
+    lib.lsv_attn_fwd_split.restype = ctypes.c_int
+    lib.lsv_attn_fwd_split_workspace_size.argtypes = [i64, i32, i32]
+    lib.lsv_attn_fwd_split_workspace_size.restype = i64
     f = ctypes.c_float
     lib.lsv_attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i32, i32, i64, i32, i32, f, vp]
     lib.lsv_attn_fwd_fp8.restype = ctypes.c_int
@@ -82,6 +90,51 @@ def lsv_attn_fwd(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, n_se
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().lsv_attn_fwd(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads,
                                        head_dim, scale, stream)
+
+
+def lsv_attn_fwd_split(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, n_seqs: int, max_seqlen: int,
+                       total_tokens: int, n_heads: int, head_dim: int, scale: float, n_split: int, workspace: int,
+                       workspace_bytes: int, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_fwd_split(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads,
+                                             head_dim, scale, n_split, workspace, workspace_bytes, stream)
+
+
+def lsv_attn_fwd_split_workspace_size(total_tokens: int, n_heads: int, n_split: int) -> int:
+    return load_library().lsv_attn_fwd_split_workspace_size(total_tokens, n_heads, n_split)
+
+
+def choose_split(seqlens, n_heads: int, compute_units: int = 256, max_split: int = 4,
+                 min_range_keys: int = 8192) -> int:
+    """The key split for ``attn_fwd_split`` (a host-side estimate from the segment lengths).
+
+    The forward runs one 256-row query tile of one (segment, head) per workgroup and one
+    workgroup per compute unit at a time; with n key ranges there are n times as many, shorter,
+    workgroups, which fill the last round better but each pay a fixed start and epilogue and
+    write fp32 partial rows that a second pass reads back. Measured on MI355X that pays only
+    while a range of the longest segment keeps at least ``min_range_keys`` keys (19,394 x 14:
+    2.53 -> 2.47 ms with 2 ranges; 4,096 x 56: 0.47 -> 0.55 ms, slower). Returns 1 when the
+    rounds are already at least 90% full, else the n in [2, max_split] with the fullest rounds
+    among those whose ranges keep ``min_range_keys`` keys (the smallest n on ties).
+    """
+    lens = [int(s) for s in seqlens if int(s) > 0]
+    if not lens:
+        return 1
+    units = sum((s + 255) // 256 for s in lens) * int(n_heads)
+
+    def fill(n):
+        work = units * n
+        return work / (math.ceil(work / compute_units) * compute_units)
+
+    if fill(1) >= 0.9:
+        return 1
+    best, best_fill = 1, fill(1)
+    for n in range(2, max_split + 1):
+        if max(lens) // n < min_range_keys:
+            break
+        if fill(n) > best_fill + 1e-9:
+            best, best_fill = n, fill(n)
+    return best
 
 
 def lsv_attn_fwd_fp8(q: int, k: int, v: int, descale_q: float, descale_k: float, descale_v: float, o: int,
@@ -188,6 +241,62 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | 
                           s.cuda_stream)
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_attn_fwd")
+    return out, lse
+
+
+def attn_fwd_split(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | None = None,
+                   n_split: int = 2, *, out=None, lse=None, workspace=None, stream=None):
+    """Attention forward with each segment's keys cut into ``n_split`` ranges (one GPU).
+
+    Arguments as for ``attn_fwd``; ``workspace``, if given, is a contiguous device buffer of at
+    least ``lsv_attn_fwd_split_workspace_size(total_tokens, heads, n_split)`` bytes (else one
+    is allocated). Returns ``(out, lse)``.
+    """
+    import torch
+    if n_split == 1:
+        return attn_fwd(q, k, v, cu_seqlens, max_seqlen, scale, out=out, lse=lse, stream=stream)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [total_tokens, heads, head_dim] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in (k, v, cu_seqlens)):
+        raise ValueError("all tensors must be on the same GPU")
+    total, heads, dim = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
+    if out.device != dev or lse.device != dev:
+        raise ValueError("out and lse must be on the same GPU as q")
+    need = lsv_attn_fwd_split_workspace_size(total, heads, n_split)
+    if need < 0:
+        raise ValueError("invalid sizes or n_split")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous buffer on the same GPU")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, max_seqlen, total, heads, dim, scale,
+                                n_split, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_fwd_split")
     return out, lse
 
 

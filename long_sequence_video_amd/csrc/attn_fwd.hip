@@ -41,6 +41,10 @@
 //  * LDS: K rows are XOR-swizzled in 16-byte chunks (conflict-free 32-row reads of one
 //    chunk); V 4-row blocks are stored column-block first (conflict-free transposing reads,
 //    and every V read address is one lane base plus an immediate).
+//  * Key-split variant (attn_fwd_split_kernel + attn_fwd_combine_kernel): the same body runs
+//    each query tile against one of n consecutive key ranges and writes that range's fp32 O and
+//    LSE; a second pass merges them per row. More, shorter workgroups fill the last round of
+//    compute units when a launch has few query tiles.
 //  * Workgroups are remapped so that consecutive tiles of one (head, segment) land on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2; each XCD's range is
 //    head-major (heads spread evenly over the XCDs), segments in packed order.
@@ -402,20 +406,38 @@ __device__ __forceinline__ void run_exact(const Ctx& cx, int n_kt, Acc& acc, con
   barrier_lds();
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
-                int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
-                int n_logical) {
+// Keys per split when a segment of seg_len keys is cut into n_split consecutive ranges: a
+// multiple of the key tile, so that every range but the last is whole tiles. Ranges that
+// start at or past seg_len are empty.
+__device__ __forceinline__ int keys_per_split(int seg_len, int n_split) {
+  return ((seg_len + n_split - 1) / n_split + kBK - 1) / kBK * kBK;
+}
+
+// One workgroup: 256 query rows of one (segment, head) against all keys of the segment, or,
+// with kSplit, against key range `split` of n_split; then O (bf16) and LSE are written, or,
+// with kSplit, this range's normalised fp32 O and its LSE into the partial buffers.
+template <bool kSplit>
+__device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                         const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                                         float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens, int n_seqs,
+                                         int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens,
+                                         float c, int n_logical, int n_split, float* __restrict__ part_o,
+                                         float* __restrict__ part_lse) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
 
   // XCD-aware order: hardware dispatches block b to XCD b % 8; give each XCD a contiguous
-  // range of logical tiles (head-major, then segment in packed order, then query tile).
+  // range of logical tiles (head-major, then segment in packed order, then key range, then
+  // query tile).
   const int per_xcd = gridDim.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (logical >= n_logical) return;
   const int qt = logical % tiles_per_seq;
-  const int hs = logical / tiles_per_seq;
+  int hs = logical / tiles_per_seq;
+  int split = 0;
+  if (kSplit) {
+    split = hs % n_split;
+    hs /= n_split;
+  }
   const int seg = hs % n_seqs;
   const int head = hs / n_seqs;
   const int seg_start = cu_seqlens[seg];
@@ -425,6 +447,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   if (seg_len > max_seqlen) return;  // breaks the contract; 32-bit copy offsets assume <= max_seqlen
   const int q0 = qt * kBQ;
   if (q0 >= seg_len) return;
+  int k0 = 0, k_len = seg_len;  // this workgroup's keys: [k0, k0 + k_len) of the segment
+  if (kSplit) {
+    const int per = keys_per_split(seg_len, n_split);
+    k0 = split * per;
+    k_len = min(per, seg_len - k0);
+    if (k_len <= 0) return;  // an empty range: the combine pass leaves it out
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -432,8 +461,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   Ctx cx;
   cx.lds_copy = lds_base + wave * kCopies * 1024;
   cx.row_stride = (unsigned)n_heads * kRowBytes;
-  cx.kbase = (const char*)k + ((int64_t)seg_start * n_heads + head) * kRowBytes;
-  cx.vbase = (const char*)v + ((int64_t)seg_start * n_heads + head) * kRowBytes;
+  cx.kbase = (const char*)k + ((int64_t)(seg_start + k0) * n_heads + head) * kRowBytes;
+  cx.vbase = (const char*)v + ((int64_t)(seg_start + k0) * n_heads + head) * kRowBytes;
   {
     const int i = tid & 63;
     row_copy_lane(wave, i, cx.krow, cx.koff);  // K: row layout
@@ -441,9 +470,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     cx.kconst = (unsigned)cx.krow * cx.row_stride + cx.koff;
     cx.vconst = (unsigned)cx.vrow * cx.row_stride + cx.voff;
   }
-  cx.seg_len = seg_len;
+  cx.seg_len = k_len;  // the key loop sees only this workgroup's key range
   cx.c = c;
-  const int n_kt = (seg_len + kBK - 1) / kBK;
+  const int n_kt = (k_len + kBK - 1) / kBK;
 
   Lane ln;
   ln.lane = tid & 63;
@@ -483,29 +512,148 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   for (int w = 0; w < kWaves; ++w) bad |= flags[w];
   if (bad) run_exact(cx, n_kt, acc, qr, ln);
 
-  // Epilogue: O / lb -> bf16, LSE = (m c + log2 l) ln 2.
+  // Epilogue: O / lb -> bf16, LSE = (m c + log2 l) ln 2; with kSplit, O / lb in fp32 and the
+  // range's LSE into the partial buffers ([split][token][head][d] and [split][head][token]).
   const float l = pair_sum(acc.l);
   const float lb = pair_sum(acc.lb);
   const int row = q0 + wave * kWaveQ + ln.l32;
   if (row < seg_len) {
     const int64_t tok = (int64_t)seg_start + row;
-    uint16_t* orow = o + (tok * n_heads + head) * kD;
+    const float lse_row = (acc.m * c + __log2f(l)) * 0.69314718055994530942f;
+    if (kSplit) {
+      float* prow = part_o + (((int64_t)split * total_tokens + tok) * n_heads + head) * kD;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x2 lo, hi;
-        lo[0] = (__bf16)(acc.O[db][4 * g + 0] / lb);
-        lo[1] = (__bf16)(acc.O[db][4 * g + 1] / lb);
-        hi[0] = (__bf16)(acc.O[db][4 * g + 2] / lb);
-        hi[1] = (__bf16)(acc.O[db][4 * g + 3] / lb);
-        u32x2 pk;
-        pk[0] = __builtin_bit_cast(unsigned, lo);
-        pk[1] = __builtin_bit_cast(unsigned, hi);
-        *(u32x2*)(orow + 32 * db + 8 * g + 4 * ln.h32) = pk;
-      }
-    if (ln.h32 == 0) lse[(int64_t)head * total_tokens + tok] = (acc.m * c + __log2f(l)) * 0.69314718055994530942f;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = acc.O[db][4 * g + e] / lb;
+          *(f32x4*)(prow + 32 * db + 8 * g + 4 * ln.h32) = w;
+        }
+      if (ln.h32 == 0) part_lse[((int64_t)split * n_heads + head) * total_tokens + tok] = lse_row;
+    } else {
+      uint16_t* orow = o + (tok * n_heads + head) * kD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x2 lo, hi;
+          lo[0] = (__bf16)(acc.O[db][4 * g + 0] / lb);
+          lo[1] = (__bf16)(acc.O[db][4 * g + 1] / lb);
+          hi[0] = (__bf16)(acc.O[db][4 * g + 2] / lb);
+          hi[1] = (__bf16)(acc.O[db][4 * g + 3] / lb);
+          u32x2 pk;
+          pk[0] = __builtin_bit_cast(unsigned, lo);
+          pk[1] = __builtin_bit_cast(unsigned, hi);
+          *(u32x2*)(orow + 32 * db + 8 * g + 4 * ln.h32) = pk;
+        }
+      if (ln.h32 == 0) lse[(int64_t)head * total_tokens + tok] = lse_row;
+    }
   }
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
+                int n_logical) {
+  fwd_body<false>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c, n_logical,
+                  1, nullptr, nullptr);
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                      const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, int n_seqs,
+                      int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c, int n_logical,
+                      int n_split, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  fwd_body<true>(q, k, v, nullptr, nullptr, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c,
+                 n_logical, n_split, part_o, part_lse);
+}
+
+// Combines the key ranges of attn_fwd_split_kernel: per (token, head) row, with LSE_s of the
+// non-empty ranges s, LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s (fp32), then
+// O -> bf16 (nearest even). One workgroup of 256 threads per (head, segment, 256-row query
+// tile), in the forward's order and with its segment checks; 16 lanes per row, 8 dims a lane.
+__global__ void __launch_bounds__(256)
+attn_fwd_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                        uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                        int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens,
+                        int n_logical, int n_split) {
+  const int logical = blockIdx.x;
+  if (logical >= n_logical) return;
+  const int qt = logical % tiles_per_seq;
+  const int hs = logical / tiles_per_seq;
+  const int seg = hs % n_seqs;
+  const int head = hs / n_seqs;
+  const int seg_start = cu_seqlens[seg];
+  const int seg_end = cu_seqlens[seg + 1];
+  if (seg_start < 0 || seg_end < seg_start || (int64_t)seg_end > total_tokens) return;
+  const int seg_len = seg_end - seg_start;
+  if (seg_len > max_seqlen) return;
+  const int q0 = qt * kBQ;
+  if (q0 >= seg_len) return;
+  const int per = keys_per_split(seg_len, n_split);
+  const int n_ranges = (seg_len + per - 1) / per;  // the non-empty ranges
+  const int j = threadIdx.x & 15;
+  const int q_end = min(q0 + kBQ, seg_len);
+  for (int row = q0 + (threadIdx.x >> 4); row < q_end; row += 16) {
+    const int64_t tok = (int64_t)seg_start + row;
+    float m = -INFINITY;
+    for (int r = 0; r < n_ranges; ++r) m = fmaxf(m, part_lse[((int64_t)r * n_heads + head) * total_tokens + tok]);
+    float sum = 0.f;
+    f32x4 a = {}, b = {};
+    for (int r = 0; r < n_ranges; ++r) {
+      const float w = __expf(part_lse[((int64_t)r * n_heads + head) * total_tokens + tok] - m);
+      sum += w;
+      const f32x4* src = (const f32x4*)(part_o + (((int64_t)r * total_tokens + tok) * n_heads + head) * kD + 8 * j);
+      const f32x4 x = src[0], y = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = __builtin_fmaf(w, x[e], a[e]);
+        b[e] = __builtin_fmaf(w, y[e], b[e]);
+      }
+    }
+    const float inv = 1.f / sum;
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      bf16x2 lo, hi;
+      lo[0] = (__bf16)(a[2 * e] * inv);
+      lo[1] = (__bf16)(a[2 * e + 1] * inv);
+      hi[0] = (__bf16)(b[2 * e] * inv);
+      hi[1] = (__bf16)(b[2 * e + 1] * inv);
+      pk[e] = __builtin_bit_cast(unsigned, lo);
+      pk[2 + e] = __builtin_bit_cast(unsigned, hi);
+    }
+    *(u32x4*)(o + (tok * n_heads + head) * kD + 8 * j) = pk;
+    if (j == 0) lse[(int64_t)head * total_tokens + tok] = m + __logf(sum);
+  }
+}
+
+constexpr int kProceed = 1;  // fwd_checks: arguments valid and there is work to launch
+constexpr int kMaxSplit = 8;
+
+// The forward's argument checks (before any HIP call): a status to return, or kProceed with the
+// number of 256-row query tiles per segment.
+int fwd_checks(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads,
+               int32_t head_dim, float scale, int64_t* tiles) {
+  if (n_seqs < 0 || max_seqlen < 0 || total_tokens < 0 || n_heads < 1) return LSV_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return LSV_ERR_INVALID_ARG;
+  if (head_dim != kD) return LSV_ERR_UNSUPPORTED;
+  if (n_seqs == 0 || max_seqlen == 0 || total_tokens == 0) return LSV_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return LSV_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return LSV_ERR_ALIGNMENT;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return LSV_ERR_ALIGNMENT;
+  if (total_tokens > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  // K/V copies address a segment with 32-bit byte offsets (rows x row stride, 24-bit factors).
+  const int64_t row_stride = (int64_t)n_heads * kRowBytes;
+  if (row_stride >= (1 << 24) || (int64_t)max_seqlen >= (1 << 24) ||
+      (int64_t)max_seqlen * row_stride + kRowBytes > (int64_t)UINT32_MAX)
+    return LSV_ERR_UNSUPPORTED;
+  *tiles = ((int64_t)max_seqlen + kBQ - 1) / kBQ;
+  return kProceed;
 }
 
 }  // namespace
@@ -543,20 +691,10 @@ int lsv_device_peak(int device, double* tflops, int* compute_units, int* clock_k
 int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                  int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
                  float scale, void* stream) {
-  if (n_seqs < 0 || max_seqlen < 0 || total_tokens < 0 || n_heads < 1) return LSV_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || !isfinite(scale)) return LSV_ERR_INVALID_ARG;
-  if (head_dim != kD) return LSV_ERR_UNSUPPORTED;
-  if (n_seqs == 0 || max_seqlen == 0 || total_tokens == 0) return LSV_OK;
-  if (!q || !k || !v || !o || !lse || !cu_seqlens) return LSV_ERR_INVALID_ARG;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return LSV_ERR_ALIGNMENT;
-  if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return LSV_ERR_ALIGNMENT;
-  if (total_tokens > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
-  // K/V copies address a segment with 32-bit byte offsets (rows x row stride, 24-bit factors).
-  const int64_t row_stride = (int64_t)n_heads * kRowBytes;
-  if (row_stride >= (1 << 24) || (int64_t)max_seqlen >= (1 << 24) ||
-      (int64_t)max_seqlen * row_stride + kRowBytes > (int64_t)UINT32_MAX)
-    return LSV_ERR_UNSUPPORTED;
-  const int64_t tiles = ((int64_t)max_seqlen + kBQ - 1) / kBQ;
+  int64_t tiles = 0;
+  const int rc = fwd_checks(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                            &tiles);
+  if (rc != kProceed) return rc;
   const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
   const int64_t grid = (n_logical + 7) / 8 * 8;
   if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
@@ -569,6 +707,50 @@ int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens,
                      (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical);
+  if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
+  return LSV_OK;
+}
+
+int64_t lsv_attn_fwd_split_workspace_size(int64_t total_tokens, int32_t n_heads, int32_t n_split) {
+  if (total_tokens < 0 || n_heads < 1 || n_split < 1 || n_split > kMaxSplit) return -1;
+  if (n_split == 1) return 0;
+  return (int64_t)n_split * total_tokens * (int64_t)n_heads * (kD + 1) * (int64_t)sizeof(float);
+}
+
+int lsv_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens,
+                       int32_t n_heads, int32_t head_dim, float scale, int32_t n_split, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  if (n_split < 1 || n_split > kMaxSplit) return LSV_ERR_INVALID_ARG;
+  if (n_split == 1)
+    return lsv_attn_fwd(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                        stream);
+  int64_t tiles = 0;
+  const int rc = fwd_checks(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                            &tiles);
+  if (rc != kProceed) return rc;
+  if (!workspace) return LSV_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 15) return LSV_ERR_ALIGNMENT;
+  if (workspace_bytes < lsv_attn_fwd_split_workspace_size(total_tokens, n_heads, n_split))
+    return LSV_ERR_INVALID_ARG;
+  const int64_t n_logical = tiles * n_split * n_seqs * (int64_t)n_heads;
+  const int64_t grid = (n_logical + 7) / 8 * 8;
+  const int64_t n_logical_c = tiles * n_seqs * (int64_t)n_heads;
+  if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute((const void*)attn_fwd_split_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return LSV_ERR_HIP;
+  float* part_o = (float*)workspace;
+  float* part_lse = part_o + (int64_t)n_split * total_tokens * n_heads * kD;
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  const hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attn_fwd_split_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen,
+                     (int)n_heads, total_tokens, c, (int)n_logical, (int)n_split, part_o, part_lse);
+  hipLaunchKernelGGL(attn_fwd_combine_kernel, dim3((unsigned)n_logical_c), dim3(256), 0, st, part_o, part_lse,
+                     (uint16_t*)o, lse, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads,
+                     total_tokens, (int)n_logical_c, (int)n_split);
   if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
   return LSV_OK;
 }

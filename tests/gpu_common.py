@@ -29,8 +29,9 @@ def from_dev(t) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_kernel(inp, device, *, out_fill=None, lse_fill=None, max_seqlen=None):
-    """Run the HIP path on an ``inputs.Inputs``; returns (out bits [T,H,D], lse [H,T])."""
+def run_kernel(inp, device, *, out_fill=None, lse_fill=None, max_seqlen=None, n_split=1):
+    """Run the HIP path on an ``inputs.Inputs`` (``lsv_attn_fwd``, or ``lsv_attn_fwd_split`` with
+    ``n_split`` key ranges); returns (out bits [T,H,D], lse [H,T])."""
     import torch
     import long_sequence_video_amd as lsv
     q, k, v = (to_dev(x, device) for x in (inp.q, inp.k, inp.v))
@@ -42,7 +43,10 @@ def run_kernel(inp, device, *, out_fill=None, lse_fill=None, max_seqlen=None):
     if lse_fill is not None:
         lse.fill_(lse_fill)
     ms = inp.max_seqlen if max_seqlen is None else max_seqlen
-    lsv.attn_fwd(q, k, v, cu, ms, inp.scale, out=out, lse=lse)
+    if n_split == 1:
+        lsv.attn_fwd(q, k, v, cu, ms, inp.scale, out=out, lse=lse)
+    else:
+        lsv.attn_fwd_split(q, k, v, cu, ms, inp.scale, n_split, out=out, lse=lse)
     torch.cuda.synchronize(device)
     return from_dev(out), lse.cpu().numpy()
 

@@ -203,3 +203,50 @@ def test_fp8_validation_before_any_hip_call(args, code):
                               a["n_seqs"], a["max_seqlen"], a["total_tokens"], a["n_heads"], a["head_dim"],
                               a["scale"], None)
     assert rc == code
+
+
+def test_split_workspace_size():
+    assert lsv.lsv_attn_fwd_split_workspace_size(19394, 14, 3) == 3 * 19394 * 14 * 129 * 4
+    assert lsv.lsv_attn_fwd_split_workspace_size(10, 2, 1) == 0
+    assert lsv.lsv_attn_fwd_split_workspace_size(0, 2, 2) == 0
+    for bad in ((10, 2, 0), (10, 2, 9), (10, 0, 2), (-1, 2, 2)):
+        assert lsv.lsv_attn_fwd_split_workspace_size(*bad) == -1
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(n_split=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_split=9), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_split=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(ws=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(ws=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(ws_bytes=2 * 10 * 4 * 129 * 4 - 1), lsv.LSV_ERR_INVALID_ARG),   # one byte short
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(scale=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(q=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(o=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(max_seqlen=299_594, total_tokens=299_594, n_heads=56, ws_bytes=1 << 42), lsv.LSV_ERR_UNSUPPORTED),
+    # successful no-ops, with any split and without a workspace
+    (dict(n_seqs=0, ws=0), lsv.LSV_OK),
+    (dict(max_seqlen=0, ws=0), lsv.LSV_OK),
+    (dict(n_split=1, n_seqs=0, ws=0), lsv.LSV_OK),
+])
+def test_split_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, n_seqs=1, max_seqlen=10, total_tokens=10, n_heads=4, head_dim=128,
+             scale=0.125, n_split=2, ws=A, ws_bytes=2 * 10 * 4 * 129 * 4)
+    a.update(args)
+    rc = lsv.lsv_attn_fwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["n_seqs"], a["max_seqlen"],
+                                a["total_tokens"], a["n_heads"], a["head_dim"], a["scale"], a["n_split"], a["ws"],
+                                a["ws_bytes"], None)
+    assert rc == code
+
+
+def test_choose_split():
+    """Host-side choice of the key split: only long segments in launches that leave the last
+    round of 256 compute units mostly idle are split."""
+    assert lsv.choose_split([19394], 14) == 2      # 1,064 workgroups (4.16 rounds) -> 2,128 (8.31)
+    assert lsv.choose_split([4096], 56) == 1       # ranges would hold under 8,192 keys
+    assert lsv.choose_split([19394, 38000, 104000], 56) == 1   # 35,392 workgroups: 99% full
+    assert lsv.choose_split([104000], 56) == 1
+    assert lsv.choose_split([38000], 56) == 1
+    assert lsv.choose_split([], 4) == 1 and lsv.choose_split([0, 0], 4) == 1
+    assert lsv.choose_split([19394], 14, min_range_keys=1024) == 4   # fullest rounds: 16.6 of 17

@@ -1,0 +1,110 @@
+"""GPU parity of the key-split forward (``lsv_attn_fwd_split``: per-range partial softmaxes in
+fp32, then a combine pass) against the fp64 oracle, through the C ABI.
+
+Same tolerances as the forward (bf16 O max-abs 2e-2, mean-abs 2e-3; LSE max-abs 1e-3). Every
+row of ragged packs for several splits, including ranges that are empty or shorter than one
+key tile; the forward's contracts (rows outside segments untouched, malformed boundaries and
+segments longer than max_seqlen skipped); determinism; the dominant-logit closed form; and
+sampled rows at the sp=4 share (19,394 x 14), the boosted-key 4,096 x 56 workload and the pack.
+"""
+
+import numpy as np
+import pytest
+
+from long_sequence_video_amd import inputs as gen
+from oracle import bf16_bits_to_f64
+from tests.gpu_common import compare, run_kernel, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n_split", [2, 3, 5, 8])
+@pytest.mark.parametrize("seqlens,heads", [
+    ([1, 0, 5, 0, 300, 2, 64], 3),
+    ([127, 128, 129], 2),
+    ([33], 2),
+    ([1000], 3),
+    ([200, 1700, 37], 2),
+])
+def test_split_all_rows(gpu, seqlens, heads, n_split):
+    inp = gen.generate(seqlens, heads, seed=700 + len(seqlens) + heads, name="split")
+    say(f"case split {n_split} {seqlens} h{heads}")
+    out, lse = run_kernel(inp, gpu, n_split=n_split)
+    compare(inp, out, lse, label=f"split {n_split} {seqlens} h{heads}")
+
+
+def test_split_many_short_segments(gpu):
+    """96 segments shorter than one 32-key tile: every split but the first is empty."""
+    rng = np.random.default_rng(31)
+    seqlens = [int(x) for x in rng.integers(1, 32, size=96)]
+    inp = gen.generate(seqlens, 2, seed=331, name="split_short")
+    say("case split short segments")
+    out, lse = run_kernel(inp, gpu, n_split=3)
+    compare(inp, out, lse, label="split short segments")
+
+
+def test_split_rows_outside_segments_untouched(gpu):
+    inp = gen.generate([100, 0, 61], 2, seed=61, total_tokens=200, name="split_poison")
+    for t in (inp.q, inp.k, inp.v):
+        t[161:] = 0x7FC0  # bf16 NaN outside every segment
+    say("case split poison")
+    out, lse = run_kernel(inp, gpu, out_fill=0x1234, lse_fill=-7.0, n_split=2)
+    assert np.all(out[161:] == 0x1234) and np.all(lse[:, 161:] == -7.0)
+    compare(inp, out, lse, rows=np.arange(161), label="split poison")
+
+
+def test_split_malformed_segments_skipped(gpu):
+    """As for the forward: a negative start, an end past total_tokens and an end before the
+    start are skipped by both passes; the valid segment is computed, other rows untouched."""
+    base = gen.generate([400], 2, seed=62, name="split_malformed")
+    bad = gen.Inputs("split_malformed", base.q, base.k, base.v, np.array([-5, 50, 170, 600, 300], np.int32),
+                     base.scale)
+    say("case split malformed")
+    out, lse = run_kernel(bad, gpu, out_fill=0x1234, lse_fill=-7.0, max_seqlen=1000, n_split=3)
+    keep = np.r_[0:50, 170:400]
+    assert np.all(out[keep] == 0x1234) and np.all(lse[:, keep] == -7.0)
+    ok = gen.Inputs("split_malformed_ok", base.q, base.k, base.v, np.array([0, 50, 170], np.int32), base.scale)
+    compare(ok, out, lse, rows=np.arange(50, 170), label="split malformed: valid segment")
+
+
+def test_split_max_seqlen_contract_and_determinism(gpu):
+    inp = gen.generate([300, 77, 150], 2, seed=63, name="split_max_seqlen")
+    say("case split max_seqlen")
+    out, lse = run_kernel(inp, gpu, n_split=2)
+    out2, lse2 = run_kernel(inp, gpu, n_split=2, max_seqlen=1000)
+    assert np.array_equal(out, out2) and np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
+    out3, lse3 = run_kernel(inp, gpu, out_fill=0x1234, lse_fill=-7.0, max_seqlen=160, n_split=2)
+    assert np.all(out3[:300] == 0x1234) and np.all(lse3[:, :300] == -7.0)
+    assert np.array_equal(out3[300:], out[300:]) and np.array_equal(lse3[:, 300:].view(np.uint32),
+                                                                      lse[:, 300:].view(np.uint32))
+
+
+def test_split_dominant_logit_gives_exact_value_row(gpu):
+    """One key far above the rest (k* = bf16(8 q), ~86 nats over random keys) placed in a late
+    range: its range's weights are exactly that V row, the other ranges' combine weights
+    vanish against it, and O is that V row bit for bit."""
+    inp = gen.generate([900], 2, seed=64, name="split_dominant")
+    i, j = 5, 850
+    qv = bf16_bits_to_f64(inp.q[i])
+    inp.k[j] = gen_bits(8.0 * qv)  # per head; exact: a power-of-two multiple of bf16 values
+    say("case split dominant")
+    out, lse = run_kernel(inp, gpu, n_split=3)
+    assert np.array_equal(out[i], inp.v[j]), "O row differs from the dominant key's V row"
+    compare(inp, out, lse, rows=np.array([i]), label="split dominant")
+
+
+def gen_bits(x):
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("name,n_split,per", [("sp4_share_s19394_h14", 3, 192), ("s4096_h56_kboost", 2, 256),
+                                              ("varlen_19394_38000_104000_h56", 2, 24)])
+def test_split_workloads_sampled(gpu, name, n_split, per):
+    import torch
+    inp = gen.make_config(name)
+    say(f"case split {n_split} {name}")
+    out, lse = run_kernel(inp, gpu, n_split=n_split)
+    compare(inp, out, lse, rows=sample_rows(inp, per, seed=11, tile=32), label=f"split {n_split} {name}")
+    torch.cuda.empty_cache()
