@@ -49,3 +49,17 @@ def test_bench_json_line(gpu):
     ref = line["mfma_reference"]  # the library GEMM calibration
     assert 0 < ref["tflops"] < 2500.0 and abs(ref["frac_of_peak"] - ref["tflops"] / 2500.0) < 1e-3
     assert abs(line["vs_library_gemm"] - line["value"] / ref["tflops"]) < 1e-3
+
+
+@pytest.mark.gpu
+def test_bench_json_line_with_key_split(gpu):
+    """The forward leg through lsv_attn_fwd_split: the line names the split and the kernels, and
+    carries no traffic figure (no counters were taken for that launch)."""
+    cmd = [sys.executable, BENCH, "--config", "tiny_s256_h4", "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+           "--no-prologue", "--no-bwd", "--no-fp8", "--no-gemm-ref", "--split", "2"]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["config"]["key_split"] == 2 and line["value"] > 0
+    assert line["roofline"]["kernel"] == "attn_fwd_split_kernel + attn_fwd_combine_kernel"
+    assert line["roofline"]["traffic"] is None
