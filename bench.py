@@ -406,7 +406,8 @@ def main():
     lse = torch.empty((inp.n_heads, inp.total_tokens), dtype=torch.float32, device=dev)
     flops = inp.flops()
     ms = inp.max_seqlen
-    n_split = lsv.choose_split(inp.seqlens, inp.n_heads) if args.split == "auto" else int(args.split)
+    _, n_cus, _ = lsv.lsv_device_peak(0)
+    n_split = lsv.choose_split(inp.seqlens, inp.n_heads, n_cus) if args.split == "auto" else int(args.split)
     ws = None
     if n_split > 1:
         ws = torch.empty(lsv.lsv_attn_fwd_split_workspace_size(inp.total_tokens, inp.n_heads, n_split),
