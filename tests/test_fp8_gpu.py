@@ -161,12 +161,19 @@ def _sampled(f8, n, seed, edge=128):
     return np.unique(np.concatenate(rows))
 
 
-@pytest.mark.parametrize("name,n", [("s4096_h56_kboost", 256), ("sp4_share_s19394_h14", 192), ("h3_s38000_h56", 48)])
-def test_fp8_workloads_sampled(gpu, name, n):
+@pytest.mark.parametrize("name", ["s4096_h56_kboost", "sp4_share_s19394_h14"])
+def test_fp8_workloads_every_row(gpu, name):
     f8 = gen.make_fp8_config(name)
-    say(f"case fp8 {name}")
+    say(f"case fp8 {name} (every row)")
     out, lse = run_fp8(f8, gpu)
-    compare_fp8(f8, out, lse, rows=_sampled(f8, n, 7), label=f"fp8 {name}")
+    compare_fp8(f8, out, lse, label=f"fp8 {name}")
+
+
+def test_fp8_38000_sampled(gpu):
+    f8 = gen.make_fp8_config("h3_s38000_h56")
+    say("case fp8 h3_s38000_h56")
+    out, lse = run_fp8(f8, gpu)
+    compare_fp8(f8, out, lse, rows=_sampled(f8, 48, 7), label="fp8 h3_s38000_h56")
 
 
 def test_fp8_varlen_pack_sampled_and_deterministic(gpu):
