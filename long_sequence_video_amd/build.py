@@ -32,8 +32,9 @@ def hipcc() -> str:
 def hip_flags() -> list[str]:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # inputs are finite by contract; lets fmaxf lower to v_max3 without NaN canonicalisation
-        "-fno-honor-nans",
+        # device code only: inputs are finite by contract, so fmaxf lowers to v_max3 without NaN
+        # canonicalisation; host code keeps IEEE semantics (its argument checks reject NaN)
+        "-Xarch_device", "-fno-honor-nans",
         # MFMA accumulators in VGPRs (the softmax reads the score accumulator on the VALU)
         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         # no packed-fp32 instructions (v_pk_*_f32) in generated code

@@ -267,13 +267,15 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
   }
 }
 
-// Runs the whole key loop with a fixed per-row reference (the max of the first tile).
-// Returns false when this lane's sums or O are not finite (a p overflowed).
+// Row sums of the bf16 P of one tile (fast path, outside the pipelined steps).
 __device__ __forceinline__ void lb_tile(Acc& acc, const bf16x8& sel, const bf16x8 (&P)[2]) {
   acc.LBm = mfma_rowsum(sel, P[0], acc.LBm);
   acc.LBm = mfma_rowsum(sel, P[1], acc.LBm);
 }
 
+// Runs the whole key loop with a fixed per-row reference (the max of the first tile).
+// Returns false when any of this lane's sums or O values is not finite (inf or NaN: a p
+// overflowed, or two overflowed products of opposite sign met in one O element).
 __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, const bf16x8 (&qr)[8],
                                          const Lane& ln, const bf16x8& sel) {
   if (n_kt >= 2) {
@@ -356,12 +358,25 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
   acc.lb = acc.LBm[0];  // lanes 32..63 hold 0: the epilogue's pair sum is the row's sum
   // No copy may still be writing this workgroup's LDS past this point.
   wait_vmcnt<0>();
-  float big = fmaxf(fabsf(acc.l), fabsf(acc.lb));
+  // Finite check of l, lb and all 64 O values on their bit patterns: a float is inf or NaN
+  // exactly when its magnitude bits are at least 0x7f800000, and magnitudes order like their
+  // bit patterns, so the integer max over all of them decides. (A float max would drop a NaN,
+  // e.g. an O element that received +inf and -inf from two late keys while l stayed finite.)
+  // The magnitude bits are taken in asm, so that nothing the build's no-NaN setting lets the
+  // compiler assume about the floats can fold the test away.
+  unsigned mag = 0;
+  auto fold = [&mag](float x) {
+    unsigned u;
+    asm("v_and_b32 %0, 0x7fffffff, %1" : "=v"(u) : "v"(x));
+    mag = max(mag, u);
+  };
+  fold(acc.l);
+  fold(acc.lb);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) big = fmaxf(big, fabsf(acc.O[db][v]));
-  return big <= 3.0e38f;  // false for inf
+    for (int v = 0; v < 16; ++v) fold(acc.O[db][v]);
+  return mag < 0x7f800000u;
 }
 
 // ---------------------------------------------------------------------------- exact path

@@ -309,6 +309,47 @@ def test_overflowing_scores_take_exact_path(gpu):
     compare(inp, out, lse, label="overflow")
 
 
+def opposite_overflow_inputs():
+    """Query row i scores 0 against every key of a 300-key segment except two, jA and jB in
+    later tiles (7 and 8 of 10), which score 32 * 31 = 992 raw units, i.e. 992 * scale * log2 e
+    = 126.5 log2 units above the first tile's max. Against that fixed reference each weight is
+    2^126.5, finite, and so are their sums l and lb (2^127.5); but v[jA, 0] = +4 and
+    v[jB, 0] = -4 make the two products +-2^128.5, which overflow to +inf and -inf in separate
+    tiles' products and leave NaN in O[i, 0] while every other O element stays finite (the other
+    dims of v[jA], v[jB] are 0.5). The exact answer: O[i, 0] = 0, O[i, d] = 0.5 for d > 0,
+    LSE = 992 scale + ln 2."""
+    L, H = 300, 2
+    inp = gen.generate([L], H, seed=24, name="opposite_overflow")
+    i, ja, jb = 5, 200, 230
+    inp.k[:, :, 0] = 0
+    for h in range(H):
+        inp.q[i, h] = 0
+        inp.q[i, h, 0] = _bits(32.0)
+        inp.k[ja, h, 0] = inp.k[jb, h, 0] = _bits(31.0)
+        inp.v[ja, h] = _bits(0.5)
+        inp.v[jb, h] = _bits(0.5)
+        inp.v[ja, h, 0] = _bits(4.0)
+        inp.v[jb, h, 0] = _bits(-4.0)
+    c = float(np.float32(inp.scale)) * np.log2(np.e)
+    assert 126.0 < 992 * c < 127.0   # finite weights and sums, overflowing products
+    return inp, i
+
+
+def test_opposite_overflows_in_one_output_element_take_exact_path(gpu):
+    """Regression: the fast path's overflow verdict must see a NaN in O (from +inf and -inf)
+    even when l, lb and every other O element are finite; the workgroup then recomputes on
+    the exact path and the row matches the oracle and its closed form."""
+    inp, i = opposite_overflow_inputs()
+    say("case opposite overflows -> exact path")
+    out, lse = run_kernel(inp, gpu)
+    got = bf16_bits_to_f64(out[i])
+    assert np.isfinite(got).all() and np.isfinite(lse).all()
+    assert np.all(got[:, 0] == 0.0) and np.all(got[:, 1:] == 0.5), got[:, :4]
+    expect = 992 * float(np.float32(inp.scale)) + np.log(2.0)
+    assert np.abs(lse[:, i] - expect).max() <= 1e-4
+    compare(inp, out, lse, label="opposite overflows")
+
+
 def test_very_negative_first_tile(gpu):
     """The first key tile scores far below the rest for every query: later p would overflow
     the first-tile reference."""

@@ -108,3 +108,16 @@ def test_split_workloads_sampled(gpu, name, n_split, per):
     out, lse = run_kernel(inp, gpu, n_split=n_split)
     compare(inp, out, lse, rows=sample_rows(inp, per, seed=11, tile=32), label=f"split {n_split} {name}")
     torch.cuda.empty_cache()
+
+
+def test_split_opposite_overflows_take_exact_path(gpu):
+    """The forward's NaN regression through the split body: with 2 ranges both overflowing
+    keys fall in the second range (keys 160..299), whose first tile scores 0 for row i."""
+    from tests.test_attention_gpu import opposite_overflow_inputs
+    inp, i = opposite_overflow_inputs()
+    say("case split opposite overflows -> exact path")
+    out, lse = run_kernel(inp, gpu, n_split=2)
+    got = bf16_bits_to_f64(out[i])
+    assert np.isfinite(got).all() and np.isfinite(lse).all()
+    assert np.abs(got[:, 0]).max() <= 1e-6 and np.abs(got[:, 1:] - 0.5).max() <= 2e-3, got[:, :4]
+    compare(inp, out, lse, label="split opposite overflows")
