@@ -5,12 +5,17 @@ partial RoPE) that feeds them.
 Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in-tree by
 ``python -m long_sequence_video_amd.build``). The functions named like the C entry points
 (``lsv_attn_fwd``, ``lsv_attn_fwd_split``, ``lsv_attn_fwd_split_workspace_size``, ``lsv_attn_fwd_fp8``,
-``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``,
-``lsv_qkv_prologue``, ``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only
-marshal arguments; ``attn_fwd``, ``attn_fwd_split``, ``attn_fwd_fp8``, ``attn_bwd`` and ``qkv_prologue`` add
-torch-tensor conveniences (shape checks, output and workspace allocation, the current
+``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``, ``lsv_qkv_prologue``,
+``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only marshal arguments;
+``attn_fwd``, ``attn_fwd_split``, ``attn_fwd_fp8``, ``attn_bwd`` and ``qkv_prologue`` add torch-tensor conveniences (shape checks, output and workspace allocation, the current
 stream). There is no fallback: if the library is missing or a call fails, an exception is
 raised.
+
+Buffers these conveniences allocate come from torch's caching allocator on the current
+stream; when the work runs on another ``stream``, each is marked as in use by that stream
+(``record_stream``), so the allocator does not hand it out again before the kernels are done.
+When ``max_seqlen`` is omitted it is computed from ``cu_seqlens`` with a device-to-host copy,
+which synchronises; the C library itself never reads ``cu_seqlens`` on the host.
 """
 
 from __future__ import annotations
@@ -28,8 +33,8 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
 EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_workspace_size", "lsv_attn_fwd_fp8",
-                    "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue", "lsv_status_string",
-                    "lsv_device_peak", "lsv_tile_config")
+                    "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak",
+                    "lsv_tile_config")
 
 LSV_OK = 0
 LSV_ERR_INVALID_ARG = -1
@@ -47,6 +52,17 @@ class LsvError(ValueError):
     def __init__(self, status: int, what: str):
         self.status = status
         super().__init__(f"{what}: {lsv_status_string(status)} (status {status})")
+
+
+def _keep_for(stream, *tensors) -> None:
+    """Mark tensors this binding allocated as in use by ``stream`` when the kernels run there
+    rather than on the current stream (torch's allocator then waits for that stream's work
+    before reusing their memory)."""
+    import torch
+    if stream != torch.cuda.current_stream(stream.device):
+        for t in tensors:
+            if t is not None:
+                t.record_stream(stream)
 
 
 def load_library(path: str = LIB_PATH):
@@ -224,10 +240,13 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | 
     if max_seqlen is None:
         cu = cu_seqlens.cpu()
         max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    mine = []
     if out is None:
         out = torch.empty_like(q)
+        mine.append(out)
     if lse is None:
         lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+        mine.append(lse)
     if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
     if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -235,6 +254,7 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | 
     if out.device != dev or lse.device != dev:
         raise ValueError("out and lse must be on the same GPU as q")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
     with torch.cuda.device(dev):
         rc = lsv_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, max_seqlen, total, heads, dim, scale,
@@ -272,10 +292,13 @@ def attn_fwd_split(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: fl
     if max_seqlen is None:
         cu = cu_seqlens.cpu()
         max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    mine = []
     if out is None:
         out = torch.empty_like(q)
+        mine.append(out)
     if lse is None:
         lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+        mine.append(lse)
     if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
     if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -287,9 +310,11 @@ def attn_fwd_split(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: fl
         raise ValueError("invalid sizes or n_split")
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        mine.append(workspace)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous buffer on the same GPU")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
     with torch.cuda.device(dev):
         rc = lsv_attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                 cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, max_seqlen, total, heads, dim, scale,
@@ -334,11 +359,14 @@ def qkv_prologue(q, k, v, q_weight, k_weight, cos, sin, *, eps: float = 1e-5, ou
     if q_weight.shape != (d,) or k_weight.shape != (d,):
         raise ValueError("norm weights must be [head_dim]")
     shape = (3, s, h, d) if q.dim() == 3 else (3 * b, s, h, d)
+    mine = []
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        mine.append(out)
     if tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != dev:
         raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {shape}")
     st = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(st, *mine)
     with torch.cuda.device(dev):
         rc = lsv_qkv_prologue(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_weight.data_ptr(), k_weight.data_ptr(),
                               0 if cos is None else cos.data_ptr(), 0 if sin is None else sin.data_ptr(),
@@ -348,22 +376,9 @@ def qkv_prologue(q, k, v, q_weight, k_weight, cos, sin, *, eps: float = 1e-5, ou
     return out
 
 
-def attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None = None, scale: float | None = None, *,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Attention backward on torch tensors (all on one GPU).
-
-    Args:
-      q, k, v, out, dout: bfloat16 ``[total_tokens, n_heads, 128]``, contiguous (``out`` and
-        ``lse`` from ``attn_fwd`` on the same q, k, v).
-      lse: float32 ``[n_heads, total_tokens]``.
-      cu_seqlens, max_seqlen, scale: as for ``attn_fwd``.
-      dq, dk, dv: optional preallocated gradients (shaped like q).
-      workspace: optional uint8 device buffer of at least ``lsv_attn_bwd_workspace_size`` bytes.
-      stream: a ``torch.cuda.Stream``; default: the current stream.
-
-    Returns:
-      ``(dq, dk, dv)``.
-    """
+def _bwd_args(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, scale, dq, dk, dv):
+    """Checks of the backward's torch arguments; returns (max_seqlen, scale, dq, dk, dv, the
+    gradient tensors allocated here)."""
     import torch
     tensors = (q, k, v, out, dout)
     if any(t.dtype != torch.bfloat16 for t in tensors):
@@ -385,21 +400,50 @@ def attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None = None,
     if max_seqlen is None:
         cu = cu_seqlens.cpu()
         max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    mine = []
+    grads = []
     for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_like(q)
+            mine.append(g)
         if g.shape != q.shape or g.dtype != torch.bfloat16 or not g.is_contiguous() or g.device != dev:
             raise ValueError("dq, dk, dv must be contiguous bfloat16 tensors shaped like q")
+        grads.append(g)
+    return max_seqlen, scale, grads[0], grads[1], grads[2], mine
+
+
+def attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None = None, scale: float | None = None, *,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward on torch tensors (all on one GPU).
+
+    Args:
+      q, k, v, out, dout: bfloat16 ``[total_tokens, n_heads, 128]``, contiguous (``out`` and
+        ``lse`` from ``attn_fwd`` on the same q, k, v).
+      lse: float32 ``[n_heads, total_tokens]``.
+      cu_seqlens, max_seqlen, scale: as for ``attn_fwd``.
+      dq, dk, dv: optional preallocated gradients (shaped like q).
+      workspace: optional uint8 device buffer of at least ``lsv_attn_bwd_workspace_size`` bytes.
+      stream: a ``torch.cuda.Stream``; default: the current stream.
+
+    Returns:
+      ``(dq, dk, dv)``.
+    """
+    import torch
+    max_seqlen, scale, dq, dk, dv, mine = _bwd_args(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, scale, dq, dk,
+                                                    dv)
+    dev = q.device
+    total, heads, dim = q.shape
     need = lsv_attn_bwd_workspace_size(total, heads)
     if need < 0:
         raise ValueError("invalid sizes")
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+        mine.append(workspace)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device buffer")
     ws_bytes = workspace.numel() * workspace.element_size()
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
     with torch.cuda.device(dev):
         rc = lsv_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
@@ -441,10 +485,13 @@ def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: floa
     if max_seqlen is None:
         cu = cu_seqlens.cpu()
         max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    mine = []
     if out is None:
         out = torch.empty((total, heads, dim), dtype=torch.bfloat16, device=dev)
+        mine.append(out)
     if lse is None:
         lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+        mine.append(lse)
     if tuple(out.shape) != (total, heads, dim) or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 [total_tokens, heads, head_dim] tensor")
     if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -452,6 +499,7 @@ def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: floa
     if out.device != dev or lse.device != dev:
         raise ValueError("out and lse must be on the same GPU as q8")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
     with torch.cuda.device(dev):
         rc = lsv_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), descale_q, descale_k, descale_v,
                               out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
