@@ -15,9 +15,15 @@ with the same flop count, against MI355X's dense FP8 peak (5.0 PFLOP/s).
 
 An object ``attn_bwd`` times the backward (dQ, dK, dV; deterministic, three kernels) on the
 same pack, counted the usual way as 2.5 x the forward's flops (the five products of the
-textbook backward); the kernels execute seven products (the dQ pass recomputes S and dP
-instead of accumulating dQ with atomics), reported as ``mfma_flops_executed``. O and LSE
-come from the forward kernel. Not part of ``value``.
+textbook backward); its roofline.frac is stated on that count. The kernels execute seven
+products (the dQ pass recomputes S and dP instead of accumulating dQ with atomics), reported
+apart as ``mfma_flops_executed`` / ``frac_executed``. O and LSE come from the forward kernel.
+Not part of ``value``.
+
+An object ``forward_legs`` times the same forward on each of the other workloads (the
+104,000-token segment of the pack alone, the 40% target row; 4,096 x 56 with boosted keys;
+the sp=4 share 19,394 x 14; 38,000 x 56; the tiny 256 x 4 case), each with its own steps and
+the same automatic key split as the headline. Not part of ``value``.
 
 A second object, ``qkv_prologue``, times the fused QKV prologue (QK RMSNorm + partial RoPE +
 V copy, the pass that feeds attention) on the same token count: 161,394 tokens x 56 heads x
@@ -226,16 +232,19 @@ def bench_backward(name: str, steps: int, warmup: int):
     executed = 3.5 * fwd
     tf = counted / (ms * 1e-3) / 1e12
     tf_exec = executed / (ms * 1e-3) / 1e12
-    log(f"{name} backward: {ms:.3f} ms, {tf:.1f} TFLOP/s counted (2.5 x fwd), {tf_exec:.1f} executed, "
-        f"{100 * tf_exec / PEAK_BF16_TFLOPS:.1f}% of peak")
+    log(f"{name} backward: {ms:.3f} ms, {tf:.1f} TFLOP/s counted (2.5 x fwd), {100 * tf / PEAK_BF16_TFLOPS:.1f}% "
+        f"of peak; {tf_exec:.1f} executed")
     del q, k, v, do, out, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return {
         "workload": name, "ms_per_step": round(ms, 4), "steps": steps,
         "tflops_counted": round(tf, 2), "flops_counted": counted, "counting": "2.5 x sum 4*S^2*H*D",
-        "mfma_flops_executed": executed,
-        "roofline": {"bound": "mfma", "achieved": round(tf_exec, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+        # The method's own work is the five products counted above; the roofline is stated on
+        # that count. The kernels also recompute S and dP in the dQ pass (seven products):
+        "mfma_flops_executed": executed, "tflops_executed": round(tf_exec, 2),
+        "frac_executed": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": "counted (2.5 x sum 4*S^2*H*D)",
                      "kernels": ["bwd_prep_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"]},
     }
 
@@ -251,6 +260,74 @@ def make_inputs(name):
     if name in EXTRA_CONFIGS:
         return gen.generate(name=name, **EXTRA_CONFIGS[name])
     raise SystemExit(f"unknown config {name!r}; known: {sorted(gen.CONFIGS) + sorted(EXTRA_CONFIGS)}")
+
+
+def time_forward(inp, steps: int, warmup: int, split="auto"):
+    """Time the forward on ``inp`` (resident in HBM): ``steps`` launches after ``warmup``, with
+    HIP events on the stream the kernels run on (torch's current stream). Returns (ms per
+    launch over the whole timed region, the sorted per-launch times, the key split used)."""
+    import torch
+    import long_sequence_video_amd as lsv
+    dev = torch.device("cuda:0")
+    to = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    q, k, v = to(inp.q), to(inp.k), to(inp.v)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((inp.n_heads, inp.total_tokens), dtype=torch.float32, device=dev)
+    ms = inp.max_seqlen
+    _, n_cus, _ = lsv.lsv_device_peak(0)
+    n_split = lsv.choose_split(inp.seqlens, inp.n_heads, n_cus) if split == "auto" else int(split)
+    ws = None
+    if n_split > 1:
+        ws = torch.empty(lsv.lsv_attn_fwd_split_workspace_size(inp.total_tokens, inp.n_heads, n_split),
+                         dtype=torch.uint8, device=dev)
+        log(f"{inp.name}: forward with {n_split} key ranges per segment (lsv_attn_fwd_split)")
+
+    def step():
+        if n_split == 1:
+            lsv.attn_fwd(q, k, v, cu, ms, inp.scale, out=out, lse=lse)
+        else:
+            lsv.attn_fwd_split(q, k, v, cu, ms, inp.scale, n_split, out=out, lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    # One event between consecutive launches: the first and last bracket the timed steps, and
+    # the ones in between give the per-launch distribution (p50 / p95).
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize(dev)
+    marks[0].record(stream)
+    for i in range(steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+    return ms_per_step, per_step, n_split
+
+
+# The forward legs of the default run: (workload, timed launches) -- about half a second of
+# GPU time each, plus a few warmup launches.
+FORWARD_LEGS = {"h56_s104000": 4, "s4096_h56_kboost": 400, "sp4_share_s19394_h14": 100, "h3_s38000_h56": 20,
+                "tiny_s256_h4": 400}
+
+
+def bench_forward_leg(name: str, split="auto"):
+    """The forward on one more workload; returns the JSON object."""
+    t0 = time.perf_counter()
+    inp = make_inputs(name)
+    gen_s = time.perf_counter() - t0
+    steps = FORWARD_LEGS.get(name, 10)
+    ms, per_step, n_split = time_forward(inp, steps, 3 if steps < 50 else 20, split)
+    tf = inp.flops() / (ms * 1e-3) / 1e12
+    log(f"{name}: {ms:.4f} ms/step, {tf:.1f} TFLOP/s, {100 * tf / PEAK_BF16_TFLOPS:.1f}% of peak "
+        f"(generated in {gen_s:.1f} s)")
+    return {"workload": name, "seqlens": inp.seqlens, "heads": inp.n_heads, "flops_per_step": inp.flops(),
+            "steps": steps, "ms_per_step": round(ms, 5), "p50_ms": round(float(np.percentile(per_step, 50)), 5),
+            "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4), "key_split": n_split}
 
 
 def cpu_baseline(inp, target_seconds: float = 15.0):
@@ -359,6 +436,7 @@ def main():
     ap.add_argument("--fp8-only", action="store_true", help="time only the FP8 forward (for profiling)")
     ap.add_argument("--bwd-only", action="store_true", help="time only the backward (for profiling)")
     ap.add_argument("--no-gemm-ref", action="store_true", help="skip the library GEMM calibration")
+    ap.add_argument("--no-legs", action="store_true", help="skip the forward legs on the other workloads")
     ap.add_argument("--gemm-ref-only", action="store_true", help="time only the library GEMM calibration")
     ap.add_argument("--split", default="auto",
                     help="key ranges per segment for the forward (lsv_attn_fwd_split): a number, or 'auto' "
@@ -380,7 +458,6 @@ def main():
     if not os.path.exists(lsv.LIB_PATH):
         from long_sequence_video_amd.build import build
         build()
-    dev = torch.device("cuda:0")
     if args.prologue_only:
         print(json.dumps({"qkv_prologue": bench_prologue(args.steps, args.warmup)}), flush=True)
         return
@@ -399,42 +476,8 @@ def main():
     t0 = time.perf_counter()
     inp = make_inputs(args.config)
     log(f"generated {args.config}: {inp.total_tokens} tokens x {inp.n_heads} heads in {time.perf_counter() - t0:.1f} s")
-    to = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
-    q, k, v = to(inp.q), to(inp.k), to(inp.v)
-    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((inp.n_heads, inp.total_tokens), dtype=torch.float32, device=dev)
     flops = inp.flops()
-    ms = inp.max_seqlen
-    _, n_cus, _ = lsv.lsv_device_peak(0)
-    n_split = lsv.choose_split(inp.seqlens, inp.n_heads, n_cus) if args.split == "auto" else int(args.split)
-    ws = None
-    if n_split > 1:
-        ws = torch.empty(lsv.lsv_attn_fwd_split_workspace_size(inp.total_tokens, inp.n_heads, n_split),
-                         dtype=torch.uint8, device=dev)
-        log(f"forward with {n_split} key ranges per segment (lsv_attn_fwd_split)")
-
-    def step():
-        if n_split == 1:
-            lsv.attn_fwd(q, k, v, cu, ms, inp.scale, out=out, lse=lse)
-        else:
-            lsv.attn_fwd_split(q, k, v, cu, ms, inp.scale, n_split, out=out, lse=lse, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
-    stream = torch.cuda.current_stream(dev)
-    # One event between consecutive launches: the first and last bracket the timed steps, and
-    # the ones in between give the per-launch distribution (p50 / p95).
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize(dev)
-    marks[0].record(stream)
-    for i in range(args.steps):
-        step()
-        marks[i + 1].record(stream)
-    torch.cuda.synchronize(dev)
-    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
-    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    ms_per_step, per_step, n_split = time_forward(inp, args.steps, args.warmup, args.split)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     log(f"{args.config}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s, {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
 
@@ -489,8 +532,9 @@ def main():
             "clock_mhz": khz // 1000,
         },
     }
-    del q, k, v, out, lse, ws
-    torch.cuda.empty_cache()
+    if not args.no_legs:
+        result["forward_legs"] = [bench_forward_leg(name, args.split) for name in FORWARD_LEGS
+                                  if name != args.config]
     if not args.no_fp8:
         result["attn_fwd_fp8"] = bench_fp8(args.config, min(max(args.steps, 3), 10), max(min(args.warmup, 2), 1))
         if not args.no_gemm_ref:

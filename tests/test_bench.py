@@ -30,7 +30,7 @@ def test_cpu_baseline_leg_reports_the_oracle_on_host_cores():
 @pytest.mark.gpu
 def test_bench_json_line(gpu):
     cmd = [sys.executable, BENCH, "--config", "tiny_s256_h4", "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
-           "--no-prologue", "--no-bwd", "--no-fp8"]
+           "--no-prologue", "--no-bwd", "--no-fp8", "--no-legs"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     line = json.loads(r.stdout.strip().splitlines()[-1])
@@ -56,10 +56,26 @@ def test_bench_json_line_with_key_split(gpu):
     """The forward leg through lsv_attn_fwd_split: the line names the split and the kernels, and
     carries no traffic figure (no counters were taken for that launch)."""
     cmd = [sys.executable, BENCH, "--config", "tiny_s256_h4", "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
-           "--no-prologue", "--no-bwd", "--no-fp8", "--no-gemm-ref", "--split", "2"]
+           "--no-prologue", "--no-bwd", "--no-fp8", "--no-gemm-ref", "--no-legs", "--split", "2"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["config"]["key_split"] == 2 and line["value"] > 0
     assert line["roofline"]["kernel"] == "attn_fwd_split_kernel + attn_fwd_combine_kernel"
     assert line["roofline"]["traffic"] is None
+
+
+@pytest.mark.gpu
+def test_forward_leg_and_backward_roofline(gpu):
+    """A forward leg reports its own timing and fraction of peak; the backward's roofline is
+    stated on the counted flops (2.5 x the forward's), the executed count apart."""
+    sys.path.insert(0, ROOT)
+    import bench
+    leg = bench.bench_forward_leg("tiny_s256_h4")
+    assert leg["workload"] == "tiny_s256_h4" and leg["steps"] == bench.FORWARD_LEGS["tiny_s256_h4"]
+    assert leg["ms_per_step"] > 0 and abs(leg["frac"] - leg["tflops"] / 2500.0) < 1e-3
+    bwd = bench.bench_backward("tiny_s256_h4", 3, 1)
+    roof = bwd["roofline"]
+    assert abs(roof["achieved"] - bwd["tflops_counted"]) < 1e-2 and abs(roof["frac"] - roof["achieved"] / 2500) < 1e-3
+    assert abs(bwd["mfma_flops_executed"] / bwd["flops_counted"] - 1.4) < 1e-12
+    assert abs(bwd["frac_executed"] - bwd["tflops_executed"] / 2500.0) < 1e-3
