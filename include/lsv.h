@@ -14,7 +14,8 @@
  * is fp32 [heads, total_tokens]; one cu_seqlens vector serves queries and keys.
  *
  * All functions are plain C, return a status (0 = success, negative = error), never
- * print, never throw, and never allocate device memory.
+ * print, never throw, and never allocate device memory (lsv_attn_bwd_noalloc's scratch array
+ * is a static device variable, set up by the HIP runtime when the code is loaded).
  */
 #ifndef LSV_H
 #define LSV_H
@@ -150,6 +151,29 @@ int lsv_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
                  int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale, void* workspace,
                  int64_t workspace_bytes, void* stream);
+
+/* lsv_attn_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving or training loops, harnesses that forbid
+ * allocation). It computes exactly what lsv_attn_bwd computes, with the same kernels and
+ * bit-identical gradients; the per-(head, token) statistics go to a scratch array that the
+ * library holds in device memory, 2^27 bytes on each GPU it runs on, kept until the process ends.
+ *
+ * Arguments as for lsv_attn_bwd, without workspace / workspace_bytes. total_tokens * n_heads
+ * must not exceed lsv_attn_bwd_noalloc_max_rows() (2^24, e.g. a 299,593-token segment at 56
+ * heads), else LSV_ERR_UNSUPPORTED before any HIP call. The first call on a device looks up
+ * that device's scratch address (a HIP runtime query, once per device); after that a call makes
+ * no allocation and no synchronisation. The scratch is fully written by each call before it is
+ * read, so nothing carries over from the previous call. Calls that overlap on one GPU (on
+ * different streams, or from several threads without ordering) share the one scratch array and
+ * race: order them on one stream.
+ */
+int lsv_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs,
+                         int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale,
+                         void* stream);
+
+/* The largest total_tokens * n_heads lsv_attn_bwd_noalloc accepts: 2^24. */
+int64_t lsv_attn_bwd_noalloc_max_rows(void);
 
 /* Fused QKV prologue on the caller's stream (asynchronous).
  *

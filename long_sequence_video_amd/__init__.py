@@ -5,9 +5,11 @@ partial RoPE) that feeds them.
 Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in-tree by
 ``python -m long_sequence_video_amd.build``). The functions named like the C entry points
 (``lsv_attn_fwd``, ``lsv_attn_fwd_split``, ``lsv_attn_fwd_split_workspace_size``, ``lsv_attn_fwd_fp8``,
-``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``, ``lsv_qkv_prologue``,
-``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only marshal arguments;
-``attn_fwd``, ``attn_fwd_split``, ``attn_fwd_fp8``, ``attn_bwd`` and ``qkv_prologue`` add torch-tensor conveniences (shape checks, output and workspace allocation, the current
+``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``, ``lsv_attn_bwd_noalloc``,
+``lsv_attn_bwd_noalloc_max_rows``, ``lsv_qkv_prologue``, ``lsv_status_string``,
+``lsv_device_peak``, ``lsv_tile_config``) only marshal arguments; ``attn_fwd``,
+``attn_fwd_split``, ``attn_fwd_fp8``, ``attn_bwd``, ``attn_bwd_noalloc`` and ``qkv_prologue``
+add torch-tensor conveniences (shape checks, output and workspace allocation, the current
 stream). There is no fallback: if the library is missing or a call fails, an exception is
 raised.
 
@@ -26,14 +28,16 @@ import os
 
 __all__ = [
     "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_workspace_size",
-    "lsv_attn_fwd_fp8", "attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue",
+    "lsv_attn_fwd_fp8", "attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_attn_bwd_noalloc",
+    "lsv_attn_bwd_noalloc_max_rows", "attn_bwd_noalloc", "lsv_qkv_prologue",
     "lsv_status_string", "lsv_device_peak", "lsv_tile_config", "attn_fwd", "attn_fwd_split", "choose_split",
     "attn_bwd", "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
 EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_workspace_size", "lsv_attn_fwd_fp8",
-                    "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak",
+                    "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_attn_bwd_noalloc",
+                    "lsv_attn_bwd_noalloc_max_rows", "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak",
                     "lsv_tile_config")
 
 LSV_OK = 0
@@ -88,6 +92,10 @@ def load_library(path: str = LIB_PATH):
     lib.lsv_attn_bwd.restype = ctypes.c_int
     lib.lsv_attn_bwd_workspace_size.argtypes = [i64, i32]
     lib.lsv_attn_bwd_workspace_size.restype = i64
+    lib.lsv_attn_bwd_noalloc.argtypes = [vp] * 10 + [i32, i32, i64, i32, i32, ctypes.c_float, vp]
+    lib.lsv_attn_bwd_noalloc.restype = ctypes.c_int
+    lib.lsv_attn_bwd_noalloc_max_rows.argtypes = []
+    lib.lsv_attn_bwd_noalloc_max_rows.restype = i64
     lib.lsv_qkv_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_float, vp]
     lib.lsv_qkv_prologue.restype = ctypes.c_int
     lib.lsv_status_string.argtypes = [ctypes.c_int]
@@ -171,6 +179,19 @@ def lsv_attn_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, d
 
 def lsv_attn_bwd_workspace_size(total_tokens: int, n_heads: int) -> int:
     return load_library().lsv_attn_bwd_workspace_size(total_tokens, n_heads)
+
+
+def lsv_attn_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+                         cu_seqlens: int, n_seqs: int, max_seqlen: int, total_tokens: int, n_heads: int,
+                         head_dim: int, scale: float, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, n_seqs, max_seqlen,
+                                               total_tokens, n_heads, head_dim, scale, stream)
+
+
+def lsv_attn_bwd_noalloc_max_rows() -> int:
+    """The largest ``total_tokens * n_heads`` that ``lsv_attn_bwd_noalloc`` accepts."""
+    return load_library().lsv_attn_bwd_noalloc_max_rows()
 
 
 def lsv_qkv_prologue(q: int, k: int, v: int, q_weight: int, k_weight: int, cos: int, sin: int, out: int,
@@ -450,6 +471,29 @@ def attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None = None,
                           max_seqlen, total, heads, dim, scale, workspace.data_ptr(), ws_bytes, s.cuda_stream)
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None = None,
+                     scale: float | None = None, *, dq=None, dk=None, dv=None, stream=None):
+    """``attn_bwd`` through ``lsv_attn_bwd_noalloc``: the library's own device scratch holds
+    the statistics, so nothing is allocated when ``dq``, ``dk`` and ``dv`` are given (and
+    ``max_seqlen``, which otherwise costs a device-to-host copy). ``total_tokens * heads``
+    must not exceed ``lsv_attn_bwd_noalloc_max_rows()``; calls that overlap on one GPU share
+    the scratch and race. Arguments and result as for ``attn_bwd``."""
+    import torch
+    max_seqlen, scale, dq, dk, dv, mine = _bwd_args(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, scale, dq, dk,
+                                                    dv)
+    dev = q.device
+    total, heads, dim = q.shape
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(),
+                                  cu_seqlens.numel() - 1, max_seqlen, total, heads, dim, scale, s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -34,6 +34,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "lsv.h"
 #include "tile_ops.h"
 
@@ -584,48 +586,85 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
-}  // namespace
+// File-scope scratch for lsv_attn_bwd_noalloc: the prep kernel's two fp32 values per (head,
+// token) for callers that cannot allocate. 2^27 bytes hold 2^24 (token, head) rows, e.g. one
+// 299,593-token segment at 56 heads, the largest the 32-bit offsets allow. Each GPU the library
+// runs on holds its own copy until the process ends. In host code the name stands for a host-side
+// shadow, not a device address: kernels get the per-device address from scratch_address().
+constexpr int64_t kScratchBytes = (int64_t)1 << 27;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
-extern "C" {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
-int64_t lsv_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads) {
-  if (total_tokens < 0 || n_heads < 1) return -1;
-  return 2 * total_tokens * (int64_t)n_heads * (int64_t)sizeof(float);
+// The device address of `scratch` on the device that `stream` belongs to (the current device
+// for the null stream), looked up once per device with that device current.
+int scratch_address(hipStream_t stream, float** out) {
+  int dev = 0;
+  if (stream == nullptr) {
+    if (hipGetDevice(&dev) != hipSuccess) return LSV_ERR_HIP;
+  } else if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    return LSV_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return LSV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return LSV_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return LSV_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return LSV_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return LSV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (float*)g_scratch_ptr[dev];
+  return LSV_OK;
 }
 
-int lsv_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                 void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
-                 int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale, void* workspace,
-                 int64_t workspace_bytes, void* stream) {
+constexpr int kProceed = 1;  // bwd_checks: arguments valid and there is work to launch
+
+// The backward's argument checks, before any HIP call (the workspace aside): a status to
+// return, or kProceed.
+int bwd_checks(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+               int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale) {
   if (n_seqs < 0 || max_seqlen < 0 || total_tokens < 0 || n_heads < 1) return LSV_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return LSV_ERR_INVALID_ARG;
   if (head_dim != kD) return LSV_ERR_UNSUPPORTED;
   if (n_seqs == 0 || max_seqlen == 0 || total_tokens == 0) return LSV_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens || !workspace)
-    return LSV_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens) return LSV_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
        (uintptr_t)dk | (uintptr_t)dv) & 15)
     return LSV_ERR_ALIGNMENT;
-  if (((uintptr_t)lse | (uintptr_t)cu_seqlens | (uintptr_t)workspace) & 3) return LSV_ERR_ALIGNMENT;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return LSV_ERR_ALIGNMENT;
   if (total_tokens > (int64_t)INT32_MAX || total_tokens * (int64_t)n_heads >= ((int64_t)1 << 31))
     return LSV_ERR_UNSUPPORTED;
-  if (workspace_bytes < lsv_attn_bwd_workspace_size(total_tokens, n_heads)) return LSV_ERR_INVALID_ARG;
   const int64_t row_stride = (int64_t)n_heads * kRowBytes;
   if (row_stride >= (1 << 24) || (int64_t)max_seqlen >= (1 << 24) ||
       (int64_t)max_seqlen * row_stride + kRowBytes > (int64_t)UINT32_MAX)
     return LSV_ERR_UNSUPPORTED;
   const int64_t tiles = ((int64_t)max_seqlen + kBlockRows - 1) / kBlockRows;
+  if ((tiles * n_seqs * (int64_t)n_heads + 7) / 8 * 8 > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  return kProceed;
+}
+
+// The three kernels on `stream`, with the stats in ws (2 * total_tokens * n_heads floats, fully
+// overwritten by the prep kernel before the other two read them). Arguments already checked.
+int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+               int64_t total_tokens, int32_t n_heads, float scale, float* ws, hipStream_t st) {
+  const int64_t tiles = ((int64_t)max_seqlen + kBlockRows - 1) / kBlockRows;
   const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
   const int64_t grid = (n_logical + 7) / 8 * 8;
-  if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
   if (hipFuncSetAttribute((const void*)attn_bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kDqLds) !=
           hipSuccess ||
       hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kDkvLds) != hipSuccess)
     return LSV_ERR_HIP;
-  float* ws_nl = (float*)workspace;
+  float* ws_nl = ws;
   float* ws_d = ws_nl + total_tokens * (int64_t)n_heads;
-  const hipStream_t st = (hipStream_t)stream;
   const float c = (float)((double)scale * 1.4426950408889634074);
   const int64_t rows = total_tokens * (int64_t)n_heads;
   const int64_t prep_need = (rows + 15) / 16;
@@ -644,6 +683,46 @@ int lsv_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                      (int)n_logical);
   if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
   return LSV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t lsv_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads) {
+  if (total_tokens < 0 || n_heads < 1) return -1;
+  return 2 * total_tokens * (int64_t)n_heads * (int64_t)sizeof(float);
+}
+
+int lsv_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                 int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+  const int rc = bwd_checks(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, n_seqs, max_seqlen, total_tokens,
+                            n_heads, head_dim, scale);
+  if (rc != kProceed) return rc;
+  if (!workspace) return LSV_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 3) return LSV_ERR_ALIGNMENT;
+  if (workspace_bytes < lsv_attn_bwd_workspace_size(total_tokens, n_heads)) return LSV_ERR_INVALID_ARG;
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, scale,
+                    (float*)workspace, (hipStream_t)stream);
+}
+
+int64_t lsv_attn_bwd_noalloc_max_rows(void) { return kScratchBytes / (2 * (int64_t)sizeof(float)); }
+
+int lsv_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs,
+                         int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale,
+                         void* stream) {
+  const int rc = bwd_checks(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, n_seqs, max_seqlen, total_tokens,
+                            n_heads, head_dim, scale);
+  if (rc != kProceed) return rc;
+  if (lsv_attn_bwd_workspace_size(total_tokens, n_heads) > kScratchBytes) return LSV_ERR_UNSUPPORTED;
+  float* ws = nullptr;
+  const int src = scratch_address((hipStream_t)stream, &ws);
+  if (src != LSV_OK) return src;
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, scale,
+                    ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -179,6 +179,42 @@ def test_bwd_validation_before_any_hip_call(args, code):
     assert rc == code
 
 
+def test_bwd_noalloc_max_rows():
+    """The no-alloc backward's scratch holds two fp32 values for 2^24 (token, head) rows: one
+    segment of 299,593 tokens at 56 heads, the largest the 32-bit offsets allow, fits."""
+    assert lsv.lsv_attn_bwd_noalloc_max_rows() == 1 << 24
+    assert 299_593 * 56 <= lsv.lsv_attn_bwd_noalloc_max_rows()
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_seqs=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(o=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dq=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dv=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(lse=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    # beyond the scratch: one (token, head) row more than 2^24
+    (dict(total_tokens=(1 << 24) + 1, n_heads=1, max_seqlen=10), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(total_tokens=299_594, n_heads=56, max_seqlen=10), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(max_seqlen=299_594, total_tokens=299_594, n_heads=56), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(n_seqs=0), lsv.LSV_OK),
+    (dict(max_seqlen=0), lsv.LSV_OK),
+    (dict(total_tokens=0), lsv.LSV_OK),
+])
+def test_bwd_noalloc_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, cu=A, n_seqs=1, max_seqlen=10, total_tokens=10,
+             n_heads=4, head_dim=128, scale=0.125)
+    a.update(args)
+    rc = lsv.lsv_attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                  a["cu"], a["n_seqs"], a["max_seqlen"], a["total_tokens"], a["n_heads"],
+                                  a["head_dim"], a["scale"], None)
+    assert rc == code
+
+
 @pytest.mark.parametrize("args,code", [
     (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
     (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
