@@ -10,8 +10,11 @@ outputs) on 1,000-4,096-token cases, which reaches 5.3e-3 (max) and 6.2e-3 (mean
 where the floor f = 1e-3 * scale * max|dO| * max|V| * max(max|Q|, max|K|) for dQ and dK and
 1e-3 * max|dO| for dV is the natural size of a term of that gradient (it matters only when
 the exact gradient vanishes, e.g. dQ and dK of a single-key segment).
-Small packs are checked on every row; larger ones on sampled rows; the full 161,394-token
-pack checks bit-exact properties (determinism, segment isolation).
+Small packs and the 4,096 x 56 and 19,394 x 14 workloads are checked on every row. At
+38,000 x 56, on the 161,394-token pack and at the largest supported segment (299,593 x 56)
+the launch covers every head and a few heads are checked on sampled rows (the first and last
+32-row tiles of every segment plus random rows); the pack also checks bit-exact properties
+(determinism, segment isolation).
 """
 
 import numpy as np
@@ -57,17 +60,22 @@ def run_bwd(inp, do, device, *, out_bits=None, lse=None, fill=None, max_seqlen=N
     return tuple(from_dev(g) for g in grads)
 
 
-def compare(inp, do, grads, *, q_rows=None, k_rows=None, label="", only=("dq", "dk", "dv")):
-    ref = attention_bwd_fp64(inp.q, inp.k, inp.v, do, inp.cu_seqlens, inp.scale, q_rows=q_rows, k_rows=k_rows)
+def compare(inp, do, grads, *, q_rows=None, k_rows=None, label="", only=("dq", "dk", "dv"), ref=None,
+            heads=None):
+    """Checks the kernel's gradients against the oracle's (computed here unless ``ref`` is given,
+    then on the sub-problem of ``heads``: ref's head h is the kernel's head heads[h])."""
+    if ref is None:
+        ref = attention_bwd_fp64(inp.q, inp.k, inp.v, do, inp.cu_seqlens, inp.scale, q_rows=q_rows, k_rows=k_rows)
+    hs = list(range(inp.n_heads)) if heads is None else list(heads)
     stats = {}
-    mx = lambda x: float(np.abs(bf16_bits_to_f64(x)).max(initial=0.0))  # noqa: E731
+    mx = lambda x: float(np.abs(bf16_bits_to_f64(x[:, hs])).max(initial=0.0))  # noqa: E731
     f_qk = 1e-3 * float(np.float32(inp.scale)) * mx(do) * mx(inp.v) * max(mx(inp.q), mx(inp.k))
     floors = {"dq": f_qk, "dk": f_qk, "dv": 1e-3 * mx(do)}
     for name, got_bits, rows in (("dq", grads[0], ref["q_rows"]), ("dk", grads[1], ref["k_rows"]),
                                  ("dv", grads[2], ref["k_rows"])):
         if name not in only:
             continue
-        got = bf16_bits_to_f64(got_bits[rows])
+        got = bf16_bits_to_f64(got_bits[rows][:, hs])
         r = ref[name]
         err = np.abs(got - r)
         fl = max(floors[name], 1e-30)
@@ -188,24 +196,59 @@ def test_sp4_share_every_row(gpu):
     compare(inp, do, grads, label="bwd sp4_share_s19394_h14")
 
 
-def test_full_pack_segment_isolation_bit_exact(gpu):
-    """The 161,394-token pack (O and LSE from the HIP forward: this checks a property of the
-    backward, not values): the 104,000-token segment's gradients equal those of that
-    segment run alone, bit for bit, and a second run is bit-identical."""
+def sampled_bwd(inp, do, device, heads, rows, label):
+    """The backward over every head of ``inp`` in one launch, checked on ``heads`` at ``rows``
+    (query rows for dQ, key rows for dK and dV). The oracle runs first, on those heads only;
+    its fp64 O and LSE, rounded to bf16 and fp32, are the kernel's O / LSE inputs for those
+    heads, as in the other parity tests. The other heads get the HIP forward's O and LSE (they
+    are part of the launch, not of the check). Returns the gradients and their stats."""
     import torch
     import long_sequence_video_amd as lsv
-    inp = gen.make_config("varlen_19394_38000_104000_h56")
-    do = _dout(inp, 1005)
-    say("case bwd varlen pack: forward")
-    q, k, v = (to_dev(x, gpu) for x in (inp.q, inp.k, inp.v))
-    cu = torch.from_numpy(inp.cu_seqlens).to(gpu)
+    hs = list(heads)
+    sub = lambda x: np.ascontiguousarray(x[:, hs])  # noqa: E731
+    say(f"case {label}: oracle on heads {hs}, {len(rows)} sampled rows")
+    ref = attention_bwd_fp64(sub(inp.q), sub(inp.k), sub(inp.v), sub(do), inp.cu_seqlens, inp.scale, q_rows=rows,
+                             k_rows=rows, return_forward=True)
+    say(f"case {label}: HIP forward for the other heads")
+    q, k, v = (to_dev(x, device) for x in (inp.q, inp.k, inp.v))
+    cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device)
     out, lse = lsv.attn_fwd(q, k, v, cu, inp.max_seqlen, inp.scale)
-    torch.cuda.synchronize()
+    torch.cuda.synchronize(device)
     out_bits, lse_h = from_dev(out), lse.cpu().numpy()
     del q, k, v, out, lse
     torch.cuda.empty_cache()
-    say("case bwd varlen pack: backward")
-    g1 = run_bwd(inp, do, gpu, out_bits=out_bits, lse=lse_h)
+    covered = np.concatenate([np.arange(a, b) for a, b in zip(inp.cu_seqlens[:-1], inp.cu_seqlens[1:])])
+    for i, h in enumerate(hs):
+        out_bits[covered, h] = gen.f64_to_bf16_bits(ref["o"][covered, i])
+        lse_h[h, covered] = ref["lse"][i, covered].astype(np.float32)
+    say(f"case {label}: HIP backward")
+    grads = run_bwd(inp, do, device, out_bits=out_bits, lse=lse_h)
+    stats = compare(inp, do, grads, label=label, ref=ref, heads=hs)
+    torch.cuda.empty_cache()
+    return grads, out_bits, lse_h, stats
+
+
+def test_h3_38000_sampled_rows(gpu):
+    """38,000 x 56 with RMS-normalised Q and K, in the bench's launch configuration: the first
+    and last 32-row tiles and 256 random rows of dQ, dK and dV on three heads (the first, a middle
+    and the last), against the oracle."""
+    from tests.gpu_common import sample_rows
+    inp = gen.make_config("h3_s38000_h56")
+    do = _dout(inp, 1004)
+    sampled_bwd(inp, do, gpu, (0, 27, 55), sample_rows(inp, 256, seed=40, tile=32), "bwd h3_s38000_h56")
+
+
+def test_full_pack_sampled_rows_and_bit_exact(gpu):
+    """The 161,394-token pack: dQ, dK and dV of two heads against the oracle on the first and last
+    32-row tiles and 128 random rows of every segment (the 104,000-token one included); then
+    bit-exact properties over all heads: a second run is bit-identical, and the 104,000-token
+    segment's gradients equal those of that segment run alone."""
+    import torch
+    from tests.gpu_common import sample_rows
+    inp = gen.make_config("varlen_19394_38000_104000_h56")
+    do = _dout(inp, 1005)
+    g1, out_bits, lse_h, _ = sampled_bwd(inp, do, gpu, (3, 41), sample_rows(inp, 128, seed=41, tile=32),
+                                         "bwd varlen pack")
     say("case bwd varlen pack: again")
     g2 = run_bwd(inp, do, gpu, out_bits=out_bits, lse=lse_h)
     for x, y in zip(g1, g2):
@@ -219,4 +262,20 @@ def test_full_pack_segment_isolation_bit_exact(gpu):
         assert np.array_equal(x[a:b], y)
     for g in g1:
         assert np.isfinite(bf16_bits_to_f64(g)).all()
+    torch.cuda.empty_cache()
+
+
+def test_largest_supported_segment(gpu):
+    """One segment of 299,593 tokens x 56 heads, the largest the kernels' 32-bit in-segment
+    offsets allow (max_seqlen * heads * 256 + 256 < 2^32; one token more is rejected on the
+    host): dQ, dK and dV of the last head (the highest addresses) against the oracle on the
+    first and last 32-row tiles and 64 random rows."""
+    import torch
+    from tests.gpu_common import sample_rows
+    n = 299_593
+    assert n * 56 * 256 + 256 < 2 ** 32 <= (n + 1) * 56 * 256 + 256
+    inp = gen.generate([n], 56, seed=1006, name="max_segment_s299593_h56")
+    do = _dout(inp, 1006)
+    sampled_bwd(inp, do, gpu, (55,), sample_rows(inp, 64, seed=42, tile=32), "bwd max segment 299593 x 56")
+    del inp, do
     torch.cuda.empty_cache()

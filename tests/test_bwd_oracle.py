@@ -131,3 +131,28 @@ def test_b6_row_subsets_and_edges():
         attention_bwd_fp64(inp.q, inp.k, inp.v, do[:5], inp.cu_seqlens, inp.scale)
     with pytest.raises(ValueError):
         attention_bwd_fp64(inp.q, inp.k, inp.v, do, inp.cu_seqlens, inp.scale, q_rows=np.array([33 + 0, 500]))
+
+
+def test_b7_forward_outputs_and_thread_count():
+    """``return_forward`` gives the forward oracle's O and LSE on every row of the segments it
+    touched, zeros elsewhere; the gradients do not depend on the thread count or on how rows
+    are split into blocks (a long segment is spread over threads block by block)."""
+    import oracle.attention_bwd as ob
+    inp, do = _case([300, 0, 45], 2, seed=21)
+    inp = gen.Inputs("b7", inp.q, inp.k, inp.v, inp.cu_seqlens, inp.scale)
+    q_rows = np.array([0, 7, 299, 300, 344])
+    k_rows = np.array([3, 150, 301])
+    one = attention_bwd_fp64(inp.q, inp.k, inp.v, do, inp.cu_seqlens, inp.scale, q_rows=q_rows, k_rows=k_rows,
+                             workers=1, return_forward=True)
+    o, l, rows = attention_fp64(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.scale)
+    np.testing.assert_allclose(one["o"][rows], o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(one["lse"][:, rows], l, rtol=1e-12, atol=1e-14)
+    old = ob._ELEMS
+    try:
+        ob._ELEMS = 300 * 8          # blocks of 8 rows: many blocks, many threads
+        many = attention_bwd_fp64(inp.q, inp.k, inp.v, do, inp.cu_seqlens, inp.scale, q_rows=q_rows,
+                                  k_rows=k_rows, workers=4)
+    finally:
+        ob._ELEMS = old
+    for name in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(many[name], one[name], rtol=1e-12, atol=1e-14)

@@ -13,36 +13,39 @@ MUTANTS = ["no_delta", "delta_sign", "dq_no_scale", "dk_no_scale", "dv_uses_dS",
 
 
 def _make(mistake):
+    """Replacements for the oracle's three steps (statistics, dQ rows, dK/dV rows), each with the
+    planted mistake where it belongs and the plain arithmetic elsewhere."""
     real_stats = ob._stats
 
-    def one(q, k, v, do, a, b, h, q_rows, k_rows, sigma):
-        qs = ob.bf16_bits_to_f64(q[a:b, h, :])
-        ks = ob.bf16_bits_to_f64(k[a:b, h, :])
-        vs = ob.bf16_bits_to_f64(v[a:b, h, :])
-        dos = ob.bf16_bits_to_f64(do[a:b, h, :])
-        lse, dvec = real_stats(qs, ks, vs, dos, sigma)
+    def stats(hd, r0, r1, sigma, keep_o):
+        real_stats(hd, r0, r1, sigma, keep_o)
         if mistake == "no_delta":
-            dvec = np.zeros_like(dvec)
+            hd.dvec[r0:r1] = 0.0
         if mistake == "delta_sign":
-            dvec = -dvec
-        iq = q_rows - a
-        p = np.exp((qs[iq] @ ks.T) * sigma - lse[iq, None])
-        ds = p * (dos[iq] @ vs.T - dvec[iq, None])
-        dq = (1.0 if mistake == "dq_no_scale" else sigma) * (ds @ (vs if mistake == "dq_uses_v" else ks))
-        ik = k_rows - a
-        pt = np.exp((ks[ik] @ qs.T) * sigma - lse[None, :])
+            hd.dvec[r0:r1] = -hd.dvec[r0:r1]
+
+    def dq(hd, idx, sigma):
+        p = np.exp((hd.qs[idx] @ hd.ks.T) * sigma - hd.lse[idx, None])
+        ds = p * (hd.dos[idx] @ hd.vs.T - hd.dvec[idx, None])
+        return (1.0 if mistake == "dq_no_scale" else sigma) * (ds @ (hd.vs if mistake == "dq_uses_v" else hd.ks))
+
+    def dkdv(hd, idx, sigma):
+        pt = np.exp((hd.ks[idx] @ hd.qs.T) * sigma - hd.lse[None, :])
         if mistake == "transpose_p":
-            pt = np.exp((qs[ik] @ ks.T) * sigma - lse[ik, None])
-        dst = pt * (vs[ik] @ dos.T - dvec[None, :])
-        dv = (dst if mistake == "dv_uses_dS" else pt) @ dos
-        dk = (1.0 if mistake == "dk_no_scale" else sigma) * ((pt if mistake == "dk_uses_p" else dst) @ qs)
-        return dq, dk, dv
-    return one
+            pt = np.exp((hd.qs[idx] @ hd.ks.T) * sigma - hd.lse[idx, None])
+        dst = pt * (hd.vs[idx] @ hd.dos.T - hd.dvec[None, :])
+        dv = (dst if mistake == "dv_uses_dS" else pt) @ hd.dos
+        dk = (1.0 if mistake == "dk_no_scale" else sigma) * ((pt if mistake == "dk_uses_p" else dst) @ hd.qs)
+        return dk, dv
+    return stats, dq, dkdv
 
 
 @pytest.mark.parametrize("mistake", MUTANTS)
 def test_pins_catch_mutant(mistake, monkeypatch):
-    monkeypatch.setattr(ob, "_one", _make(mistake))
+    stats, dq, dkdv = _make(mistake)
+    monkeypatch.setattr(ob, "_stats", stats)
+    monkeypatch.setattr(ob, "_dq", dq)
+    monkeypatch.setattr(ob, "_dkdv", dkdv)
     caught = 0
     for t in PIN_TESTS:
         try:
@@ -50,3 +53,13 @@ def test_pins_catch_mutant(mistake, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught > 0, f"no pin caught mutant {mistake!r}"
+
+
+def test_unmutated_steps_pass_the_pins(monkeypatch):
+    """The replacement steps with no mistake are the oracle itself: every pin passes."""
+    stats, dq, dkdv = _make("none")
+    monkeypatch.setattr(ob, "_stats", stats)
+    monkeypatch.setattr(ob, "_dq", dq)
+    monkeypatch.setattr(ob, "_dkdv", dkdv)
+    for t in PIN_TESTS:
+        t()
