@@ -53,6 +53,15 @@ int lsvgen_choose(int64_t* out, int64_t n_choose, int64_t n_total, int64_t* work
  * rounding to bf16 (exact for a power of two unless it overflows). */
 int lsvgen_scale_rows_bf16(uint16_t* x, const int64_t* rows, int64_t n_rows, int64_t row_len, float factor);
 
+/* out[i] = OCP FP8 e4m3 bits of x[i] / descale (division in double; rounded to nearest, ties
+ * to even, in the binade of the quotient, subnormal spacing 2^-9, saturating at +-448). The
+ * per-tensor quantisation of the FP8 workloads (descale = fp32(amax / 448)). Returns -1 for
+ * a negative n, null pointers or a descale that is not finite and positive. */
+int lsvgen_quantize_e4m3_bf16(const uint16_t* x, int64_t n, double descale, uint8_t* out);
+
+/* *amax = the largest |x[i]| of n bf16 values (0 for n = 0). */
+int lsvgen_amax_bf16(const uint16_t* x, int64_t n, double* amax);
+
 /* Element e of the (seed, tensor) normal stream as a double, before any rounding. */
 double lsvgen_normal_f64_at(uint64_t seed, uint32_t tensor, int64_t e);
 

@@ -66,8 +66,10 @@ def _load():
     lib.lsvgen_scale_rows_bf16.argtypes = [u16p, i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float]
     lib.lsvgen_normal_f64_at.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64]
     lib.lsvgen_normal_f64_at.restype = ctypes.c_double
+    lib.lsvgen_quantize_e4m3_bf16.argtypes = [u16p, ctypes.c_int64, ctypes.c_double, ctypes.POINTER(ctypes.c_uint8)]
+    lib.lsvgen_amax_bf16.argtypes = [u16p, ctypes.c_int64, ctypes.POINTER(ctypes.c_double)]
     for f in (lib.lsvgen_normal_bf16, lib.lsvgen_rms_normalize_bf16, lib.lsvgen_choose,
-              lib.lsvgen_scale_rows_bf16):
+              lib.lsvgen_scale_rows_bf16, lib.lsvgen_quantize_e4m3_bf16, lib.lsvgen_amax_bf16):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -371,16 +373,35 @@ class Fp8Inputs:
         return float(sum(4.0 * s * s * self.n_heads * self.q.shape[2] for s in self.seqlens))
 
 
+def amax_bf16(bits: np.ndarray) -> float:
+    """The largest |x| of a bf16 array (uint16 bit patterns)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = ctypes.c_double()
+    _check(_load().lsvgen_amax_bf16(b.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), b.size, ctypes.byref(out)),
+           "amax_bf16")
+    return out.value
+
+
+def quantize_e4m3_bf16(bits: np.ndarray, descale: float) -> np.ndarray:
+    """e4m3 bits of bf16 values / descale (the C generator; equal to
+    ``f64_to_e4m3_bits(x / descale)``, without float64 temporaries), same shape."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.uint8)
+    _check(_load().lsvgen_quantize_e4m3_bf16(b.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), b.size,
+                                               float(descale), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))),
+           "quantize_e4m3_bf16")
+    return out
+
+
 def quantize_fp8(inp: Inputs, name: str | None = None) -> Fp8Inputs:
     """Per-tensor e4m3 quantisation of a bf16 workload: descale = fp32(amax / 448), values
     x / descale rounded to e4m3 (the usual amax recipe for FP8 attention inputs)."""
     out = {}
     for key in ("q", "k", "v"):
         bits = getattr(inp, key)
-        xf = (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        amax = float(np.abs(xf).max()) or 1.0
+        amax = amax_bf16(bits) or 1.0
         d = float(np.float32(amax / E4M3_MAX))
-        out[key] = (f64_to_e4m3_bits(xf / d), d)
+        out[key] = (quantize_e4m3_bf16(bits, d), d)
     return Fp8Inputs(name or inp.name + "_fp8", out["q"][0], out["k"][0], out["v"][0], out["q"][1], out["k"][1],
                      out["v"][1], inp.cu_seqlens, inp.scale, dict(inp.meta))
 

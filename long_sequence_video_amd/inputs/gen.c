@@ -139,3 +139,54 @@ double lsvgen_normal_f64_at(uint64_t seed, uint32_t tensor, int64_t e) {
   normal_pair(stream_start(seed, tensor), (uint64_t)(e / 2), &z0, &z1);
   return (e & 1) ? z1 : z0;
 }
+
+/* Per-tensor e4m3 quantisation of bf16 values: out[i] = e4m3(x[i] / descale), OCP FP8 E4M3
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities), rounded to nearest
+ * with ties to even in the binade of |y| (subnormal spacing 2^-9 below 2^-6), saturating at
+ * 448; the division is done in double. Exactly what inputs.f64_to_e4m3_bits gives for
+ * x / descale, without its float64 temporaries. */
+int lsvgen_quantize_e4m3_bf16(const uint16_t* x, int64_t n, double descale, uint8_t* out) {
+  if (n < 0 || (n > 0 && (!x || !out)) || !(descale > 0.0) || !isfinite(descale)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const double y = (double)bf16_to_f32(x[i]) / descale;
+    const uint8_t sign = signbit(y) ? 0x80 : 0;
+    double a = fabs(y);
+    if (a > 448.0) a = 448.0;
+    uint8_t bits = 0;
+    if (a > 0.0) {
+      int ex;
+      frexp(a, &ex);             /* a = f 2^ex, f in [0.5, 1): the binade is 2^(ex - 1) */
+      int e = ex - 1;
+      if (e < -6) e = -6;        /* subnormals share the spacing of the lowest binade */
+      if (e > 8) e = 8;
+      const double quantum = ldexp(1.0, e - 3);
+      double r = rint(a / quantum) * quantum;   /* default rounding: to nearest, ties to even */
+      if (r > 448.0) r = 448.0;
+      if (r >= 0.015625) {       /* normal: r = (1 + m/8) 2^ee */
+        int er;
+        frexp(r, &er);
+        const int ee = er - 1;
+        const int mant = (int)(ldexp(r, -ee) * 8.0 - 8.0);
+        bits = (uint8_t)(((ee + 7) << 3) | mant);
+      } else {                   /* subnormal: r = m 2^-9 */
+        bits = (uint8_t)(int)ldexp(r, 9);
+      }
+    }
+    out[i] = (uint8_t)(bits | sign);
+  }
+  return 0;
+}
+
+/* The largest |x| over n bf16 values, as a double (0 for n = 0). */
+int lsvgen_amax_bf16(const uint16_t* x, int64_t n, double* amax) {
+  if (n < 0 || (n > 0 && !x) || !amax) return -1;
+  uint16_t m = 0;
+#pragma omp parallel for reduction(max : m) schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const uint16_t u = (uint16_t)(x[i] & 0x7FFF);   /* magnitudes order like their bit patterns */
+    if (u > m) m = u;
+  }
+  *amax = (double)bf16_to_f32(m);
+  return 0;
+}

@@ -23,6 +23,9 @@ bits; exponent field 0 is subnormal (m * 2^-9); no infinities; S.1111.111 is NaN
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .attention import f32_to_f64, segments
@@ -50,7 +53,7 @@ def e4m3_bits_to_f64(bits) -> np.ndarray:
 
 
 def attention_fp8_fp64(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, cu_seqlens,
-                       scale: float, *, rows=None):
+                       scale: float, *, rows=None, workers: int | None = None):
     """Reference FP8 attention forward in fp64.
 
     Args:
@@ -58,6 +61,7 @@ def attention_fp8_fp64(q8, k8, v8, descale_q: float, descale_k: float, descale_v
       descale_q, descale_k, descale_v, scale: fp32 values (widened exactly).
       cu_seqlens: ``[n_seqs + 1]`` segment boundaries starting at 0.
       rows: optional sorted token indices (default: every covered token).
+      workers: threads over (segment, head) pairs; default: all usable cores.
 
     Returns:
       ``(out [R, H, D], lse [H, R], rows)``.
@@ -76,22 +80,35 @@ def attention_fp8_fp64(q8, k8, v8, descale_q: float, descale_k: float, descale_v
     out = np.zeros((len(rows), n_heads, d))
     lse = np.zeros((n_heads, len(rows)))
     covered = np.zeros(len(rows), bool)
+    jobs = []
     for a, b in segs:
         lo, hi = np.searchsorted(rows, a), np.searchsorted(rows, b)
         if hi == lo:
             continue
         covered[lo:hi] = True
-        idx = rows[lo:hi]
-        for h in range(n_heads):
-            qs = dq * e4m3_bits_to_f64(q8[idx, h])          # real query rows
-            ks = dk * e4m3_bits_to_f64(k8[a:b, h])          # real keys of the segment
-            vs = dv * e4m3_bits_to_f64(v8[a:b, h])
-            z = sigma * (qs @ ks.T)
-            m = z.max(axis=1)
-            e = np.exp(z - m[:, None])
-            l = e.sum(axis=1)
-            out[lo:hi, h] = (e @ vs) / l[:, None]
-            lse[h, lo:hi] = m + np.log(l)
+        jobs += [(a, b, h, lo, hi) for h in range(n_heads)]
     if not covered.all():
         raise ValueError("every requested row must lie inside a segment")
+
+    def run(job):
+        a, b, h, lo, hi = job
+        idx = rows[lo:hi]
+        qs = dq * e4m3_bits_to_f64(q8[idx, h])          # real query rows
+        ks = dk * e4m3_bits_to_f64(k8[a:b, h])          # real keys of the segment
+        vs = dv * e4m3_bits_to_f64(v8[a:b, h])
+        z = sigma * (qs @ ks.T)
+        m = z.max(axis=1)
+        e = np.exp(z - m[:, None])
+        l = e.sum(axis=1)
+        out[lo:hi, h] = (e @ vs) / l[:, None]
+        lse[h, lo:hi] = m + np.log(l)
+
+    n = workers or len(os.sched_getaffinity(0))
+    if n <= 1 or len(jobs) <= 1:
+        for j in jobs:
+            run(j)
+    else:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(n) as ex:
+            list(ex.map(run, jobs))
     return out, lse, rows

@@ -36,8 +36,8 @@ def test_generator_library_exports_every_declared_symbol():
     from long_sequence_video_amd import inputs as gen
     text = re.sub(r"/\*.*?\*/", "", open(GEN_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(lsvgen_\w+)\s*\(", text)))
-    assert names == ["lsvgen_choose", "lsvgen_normal_bf16", "lsvgen_normal_f64_at", "lsvgen_rms_normalize_bf16",
-                     "lsvgen_scale_rows_bf16"]
+    assert names == ["lsvgen_amax_bf16", "lsvgen_choose", "lsvgen_normal_bf16", "lsvgen_normal_f64_at",
+                     "lsvgen_quantize_e4m3_bf16", "lsvgen_rms_normalize_bf16", "lsvgen_scale_rows_bf16"]
     lib = ctypes.CDLL(gen.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -51,6 +51,13 @@ def test_generator_rejects_bad_arguments():
     assert lib.lsvgen_normal_bf16(None, ctypes.c_int64(0), ctypes.c_uint64(1), ctypes.c_uint32(0)) == 0
     assert lib.lsvgen_choose(None, ctypes.c_int64(3), ctypes.c_int64(2), None, ctypes.c_uint64(1),
                              ctypes.c_uint32(3)) == -1
+    u8 = (ctypes.c_uint8 * 4)()
+    u16 = (ctypes.c_uint16 * 4)()
+    assert lib.lsvgen_quantize_e4m3_bf16(u16, ctypes.c_int64(4), ctypes.c_double(0.0), u8) == -1
+    assert lib.lsvgen_quantize_e4m3_bf16(u16, ctypes.c_int64(4), ctypes.c_double(float("nan")), u8) == -1
+    assert lib.lsvgen_quantize_e4m3_bf16(None, ctypes.c_int64(4), ctypes.c_double(1.0), u8) == -1
+    assert lib.lsvgen_quantize_e4m3_bf16(u16, ctypes.c_int64(-1), ctypes.c_double(1.0), u8) == -1
+    assert lib.lsvgen_amax_bf16(u16, ctypes.c_int64(4), None) == -1
 
 
 def test_status_strings():

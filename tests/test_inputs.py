@@ -135,3 +135,27 @@ def test_generate_arguments():
     x = gen.generate([3, 0, 4], heads=2, head_dim=8, seed=0, total_tokens=9)
     assert x.q.shape == (9, 2, 8) and list(x.cu_seqlens) == [0, 3, 3, 7]
     assert x.max_seqlen == 4 and x.seqlens == [3, 0, 4]
+
+
+def test_c_e4m3_quantiser_equals_the_numpy_definition():
+    """The C quantiser (used for the FP8 workloads) gives the same bytes as
+    ``f64_to_e4m3_bits(x / descale)`` on random values and on the edge cases: zeros of both
+    signs, ties between two e4m3 values (to even), the subnormal range, saturation at 448."""
+    rng = np.random.default_rng(5)
+    x = gen.normal_bf16(200_000, 77, 0)
+    edges = np.array([0.0, -0.0, 448.0, -448.0, 460.0, 464.0, 1e6, 2.0 ** -6, 2.0 ** -9, 2.0 ** -10,
+                      1.5 * 2.0 ** -10, 1.0625, 1.1875, 3.0 * 2.0 ** -11, 17.0, 19.0, 240.0, 232.0, 248.0])
+    ebits = gen.f64_to_bf16_bits(np.r_[edges, -edges])
+    for descale in (1.0, 0.0123, float(np.float32(5.61 / 448.0)), 2.0 ** -7, 3.7):
+        for bits in (x, ebits, rng.integers(0, 0x7F80, 5000).astype(np.uint16)):
+            vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            want = gen.f64_to_e4m3_bits(vals / descale)
+            got = gen.quantize_e4m3_bf16(bits, descale)
+            assert np.array_equal(got, want), (descale, np.flatnonzero(got != want)[:5])
+
+
+def test_c_amax_equals_numpy():
+    x = gen.normal_bf16(100_001, 3, 1)
+    vals = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert gen.amax_bf16(x) == np.abs(vals).max()
+    assert gen.amax_bf16(np.zeros(0, np.uint16)) == 0.0
