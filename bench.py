@@ -23,12 +23,17 @@ Not part of ``value``.
 An object ``forward_legs`` times the same forward on each of the other workloads (the
 104,000-token segment of the pack alone, the 40% target row; 4,096 x 56 with boosted keys;
 the sp=4 share 19,394 x 14; 38,000 x 56; the tiny 256 x 4 case), each with its own steps and
-the same automatic key split as the headline. Not part of ``value``.
+the same automatic key split as the headline. Not part of ``value``. One more leg,
+``fallback_s38000_h56``, is 38,000 x 56 with every query's first key tile scoring far below the
+rest, so that every workgroup's fixed-reference pass overflows and reruns on the exact path;
+its ``vs_fast_path`` is its time over the plain 38,000 x 56 leg's.
 
 A second object, ``qkv_prologue``, times the fused QKV prologue (QK RMSNorm + partial RoPE +
 V copy, the pass that feeds attention) on the same token count: 161,394 tokens x 56 heads x
 128, rotary width 96. It is bound by HBM and reported in GB/s against 8 TB/s; it is not
-part of ``value``.
+part of ``value``. ``qkv_prologue_fused_q`` times prologue + forward on the pack two ways:
+the stacked prologue then the forward, and the K-only prologue then the forward that
+normalises and rotates Q in its Q-tile load (six planes of prologue traffic against two).
 
 An object ``mfma_reference`` times a plain library GEMM (torch.matmul, i.e. hipBLASLt, bf16,
 16384^3, 50 calls back to back) on the same GPU: the dense matrix throughput a tuned library
@@ -59,7 +64,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense BF16 MFMA peak (2.5 PFLOP/s)
 DEFAULT_CONFIG = "varlen_19394_38000_104000_h56"
 # The segment of the default pack that the 40% target is stated for, run alone.
-EXTRA_CONFIGS = {"h56_s104000": dict(seqlens=[104000], heads=56, seed=1005)}
+EXTRA_CONFIGS = {"h56_s104000": dict(seqlens=[104000], heads=56, seed=1005),
+                 # 38,000 x 56 with every query's first key tile ~113 nats below the rest: every
+                 # workgroup's fixed-reference pass overflows and reruns on the exact path.
+                 "fallback_s38000_h56": dict(seqlens=[38000], heads=56, seed=1004, rms_qk=True,
+                                             low_first_tile=80.0)}
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "long_sequence_video_amd", "csrc", "attn_fwd.hip")
@@ -151,6 +160,63 @@ def bench_prologue(steps: int, warmup: int):
             "traffic_source": traffic_src, "algorithmic_hbm_bytes": nbytes, "kernel": "qkv_prologue_kernel",
         },
     }
+
+
+def bench_qnorm(steps: int, warmup: int):
+    """The forward with the QKV prologue in front of it on the 161,394-token pack x 56 heads
+    (R = 96, each segment's own RoPE positions), two ways: the stacked prologue (Q, K, V planes)
+    then the forward, and lsv_norm_rope on K then the forward with Q's norm and rotation in its
+    Q-tile load. Returns the JSON object (per-part times, and the prologue bytes each way)."""
+    import torch
+    import long_sequence_video_amd as lsv
+    from long_sequence_video_amd import inputs as gen
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    inp = gen.generate_qnorm([19394, 38000, 104000], 56, 96, seed=1008, name="qnorm_varlen_161394_h56")
+    log(f"generated {inp.name} in {time.perf_counter() - t0:.1f} s")
+    to = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    q, k, v, qw, kw, cos, sin = (to(x) for x in (inp.q, inp.k, inp.v, inp.q_weight, inp.k_weight, inp.cos, inp.sin))
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    t, h = inp.total_tokens, inp.n_heads
+    stacked = torch.empty((3, t, h, 128), dtype=torch.bfloat16, device=dev)
+    kn = torch.empty_like(k)
+    out = torch.empty_like(q)
+    lse = torch.empty((h, t), dtype=torch.float32, device=dev)
+    ms = inp.max_seqlen
+    parts = {
+        "two_pass": [lambda: lsv.qkv_prologue(q, k, v, qw, kw, cos, sin, eps=inp.eps, out=stacked),
+                     lambda: lsv.attn_fwd(stacked[0], stacked[1], stacked[2], cu, ms, inp.scale, out=out, lse=lse)],
+        "fused_q": [lambda: lsv.norm_rope(k, kw, cos, sin, eps=inp.eps, out=kn),
+                    lambda: lsv.attn_fwd_qnorm(q, kn, v, qw, cos, sin, cu, ms, inp.scale, eps=inp.eps, out=out,
+                                               lse=lse)],
+    }
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, (pro, att) in parts.items():
+        for _ in range(warmup):
+            pro()
+            att()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+        torch.cuda.synchronize(dev)
+        ev[0].record(stream)
+        for i in range(steps):
+            pro()
+            ev[2 * i + 1].record(stream)
+            att()
+            ev[2 * i + 2].record(stream)
+        torch.cuda.synchronize(dev)
+        pro_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+        att_ms = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(steps)) / steps
+        res[name] = {"prologue_ms": round(pro_ms, 4), "attention_ms": round(att_ms, 4),
+                     "total_ms": round(pro_ms + att_ms, 4)}
+        log(f"{inp.name} {name}: prologue {pro_ms:.3f} ms + attention {att_ms:.3f} ms")
+    plane = t * h * 128 * 2
+    res.update({"workload": inp.name, "rotary_dim": 96, "steps": steps,
+                "prologue_hbm_bytes": {"two_pass": 6 * plane, "fused_q": 2 * plane},
+                "attention_tflops_fused_q": round(inp.flops() / (res["fused_q"]["attention_ms"] * 1e-3) / 1e12, 2)})
+    del q, k, v, qw, kw, cos, sin, stacked, kn, out, lse
+    torch.cuda.empty_cache()
+    return res
 
 
 PEAK_FP8_TFLOPS = 5000.0  # MI355X published dense FP8 MFMA peak (5.0 PFLOP/s)
@@ -276,15 +342,25 @@ def time_forward(inp, steps: int, warmup: int, split="auto"):
     lse = torch.empty((inp.n_heads, inp.total_tokens), dtype=torch.float32, device=dev)
     ms = inp.max_seqlen
     _, n_cus, _ = lsv.lsv_device_peak(0)
-    n_split = lsv.choose_split(inp.seqlens, inp.n_heads, n_cus) if split == "auto" else int(split)
     ws = None
-    if n_split > 1:
+    if split == "auto":
+        ranges, tail_tiles = lsv.lsv_attn_fwd_tail_plan(len(inp.cu_seqlens) - 1, ms, inp.n_heads, n_cus)
+        n_split = {"tail_ranges": ranges, "tail_tiles": tail_tiles} if ranges > 1 else 1
+    else:
+        n_split = int(split)
+    if isinstance(n_split, dict):
+        ws = torch.empty(lsv.lsv_attn_fwd_tail_workspace_size(n_cus), dtype=torch.uint8, device=dev)
+        log(f"{inp.name}: forward with the last round's {n_split['tail_tiles']} query tiles cut into "
+            f"{n_split['tail_ranges']} key ranges (lsv_attn_fwd_tail)")
+    elif n_split > 1:
         ws = torch.empty(lsv.lsv_attn_fwd_split_workspace_size(inp.total_tokens, inp.n_heads, n_split),
                          dtype=torch.uint8, device=dev)
         log(f"{inp.name}: forward with {n_split} key ranges per segment (lsv_attn_fwd_split)")
 
     def step():
-        if n_split == 1:
+        if isinstance(n_split, dict):
+            lsv.attn_fwd_tail(q, k, v, cu, ms, inp.scale, compute_units=n_cus, out=out, lse=lse, workspace=ws)
+        elif n_split == 1:
             lsv.attn_fwd(q, k, v, cu, ms, inp.scale, out=out, lse=lse)
         else:
             lsv.attn_fwd_split(q, k, v, cu, ms, inp.scale, n_split, out=out, lse=lse, workspace=ws)
@@ -312,7 +388,7 @@ def time_forward(inp, steps: int, warmup: int, split="auto"):
 # The forward legs of the default run: (workload, timed launches) -- about half a second of
 # GPU time each, plus a few warmup launches.
 FORWARD_LEGS = {"h56_s104000": 4, "s4096_h56_kboost": 400, "sp4_share_s19394_h14": 100, "h3_s38000_h56": 20,
-                "tiny_s256_h4": 400}
+                "tiny_s256_h4": 400, "fallback_s38000_h56": 8}
 
 
 def bench_forward_leg(name: str, split="auto"):
@@ -439,8 +515,9 @@ def main():
     ap.add_argument("--no-legs", action="store_true", help="skip the forward legs on the other workloads")
     ap.add_argument("--gemm-ref-only", action="store_true", help="time only the library GEMM calibration")
     ap.add_argument("--split", default="auto",
-                    help="key ranges per segment for the forward (lsv_attn_fwd_split): a number, or 'auto' "
-                         "(choose_split: 1 unless the launch leaves the last round of compute units mostly idle)")
+                    help="'auto': lsv_attn_fwd_tail (the last, partial round of query tiles cut into key ranges "
+                         "when that plan cuts any, else lsv_attn_fwd); or a number of key ranges for every tile "
+                         "(lsv_attn_fwd_split; 1 = lsv_attn_fwd)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward of one rank's share runs on a "
@@ -482,9 +559,14 @@ def main():
     log(f"{args.config}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s, {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
 
     peak_at_clock, cus, khz = lsv.lsv_device_peak(0)
-    if n_split == 1:
+    if isinstance(n_split, dict):
+        kernel = "attn_fwd_tail_kernel"
+        traffic, traffic_src = measured_traffic(inp.name, kernel="attn_fwd_tail")
+    elif n_split == 1:
+        kernel = "attn_fwd_kernel"
         traffic, traffic_src = measured_traffic(inp.name)
     else:
+        kernel = "attn_fwd_split_kernel + attn_fwd_combine_kernel"
         traffic, traffic_src = None, "not measured for the key-split launch"
     # HBM-minimal bytes per launch: q, k, v read once, O written once (bf16), LSE (fp32).
     algorithmic_bytes = 4 * inp.total_tokens * inp.n_heads * inp.head_dim * 2 + inp.total_tokens * inp.n_heads * 4
@@ -526,7 +608,7 @@ def main():
             "traffic_unit": "HBM bytes per launch",
             "traffic_source": traffic_src,
             "algorithmic_hbm_bytes": algorithmic_bytes,
-            "kernel": "attn_fwd_kernel" if n_split == 1 else "attn_fwd_split_kernel + attn_fwd_combine_kernel",
+            "kernel": kernel,
             "peak_at_reported_clock": round(peak_at_clock, 1),
             "compute_units": cus,
             "clock_mhz": khz // 1000,
@@ -535,6 +617,11 @@ def main():
     if not args.no_legs:
         result["forward_legs"] = [bench_forward_leg(name, args.split) for name in FORWARD_LEGS
                                   if name != args.config]
+        by_name = {leg["workload"]: leg for leg in result["forward_legs"]}
+        if "fallback_s38000_h56" in by_name and "h3_s38000_h56" in by_name:
+            # what a workload pays when every workgroup reruns on the exact path
+            by_name["fallback_s38000_h56"]["vs_fast_path"] = round(
+                by_name["fallback_s38000_h56"]["ms_per_step"] / by_name["h3_s38000_h56"]["ms_per_step"], 3)
     if not args.no_fp8:
         result["attn_fwd_fp8"] = bench_fp8(args.config, min(max(args.steps, 3), 10), max(min(args.warmup, 2), 1))
         if not args.no_gemm_ref:
@@ -546,6 +633,7 @@ def main():
         result["attn_bwd"] = bench_backward(args.config, min(max(args.steps, 3), 5), max(min(args.warmup, 2), 1))
     if not args.no_prologue:
         result["qkv_prologue"] = bench_prologue(max(args.steps, 10), max(args.warmup, 2))
+        result["qkv_prologue_fused_q"] = bench_qnorm(min(max(args.steps, 3), 5), 1)
     if not args.no_gemm_ref:
         ref = bench_gemm_reference("bf16")
         result["mfma_reference"] = ref

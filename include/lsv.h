@@ -66,6 +66,36 @@ int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
                  float scale, void* stream);
 
+/* Attention forward with the Q side of the QKV prologue fused into the Q-tile load
+ * (asynchronous, one kernel on the caller's stream).
+ *
+ * The operation: the MotionKernel qkv_prologue of FastVideo #2049 (diff of
+ * fastvideo/models/dits/minimax_h3_fusions/mk/qkv_prologue.py, module docstring and kernel;
+ * MiniMaxH3Attention.forward on the same page rotates 96 of the 128 channels) applied to q, then
+ * the varlen forward of lsv_attn_fwd. Each raw (token t, head) row x of q becomes
+ *     y_i = x_i * rsqrt(mean_d x_d^2 + eps) * q_weight_i
+ *     q'_i = y_i cos[t,i] - y_{i+R/2} sin[t,i]  (i < R/2),  y_i cos[t,i] + y_{i-R/2} sin[t,i]  (R/2 <= i < R),
+ *     q'_i = y_i  (i >= R),
+ * computed in fp32 and rounded once to bf16 -- the same steps and summation order as
+ * lsv_norm_rope and lsv_qkv_prologue, so q' is bit-identical to what they write -- and
+ * O, LSE = attention(q', k, v) exactly as lsv_attn_fwd computes it. Q is read once and never
+ * written back: the prologue's pass over Q never touches HBM. k is expected already normalised
+ * and rotated (lsv_norm_rope), v as is.
+ *
+ * q            device pointer, bf16 raw queries [total_tokens, n_heads, head_dim], 16-byte aligned.
+ * k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale, stream:
+ *              as for lsv_attn_fwd (same layouts, limits and skipped-segment rule).
+ * q_weight     device pointer, bf16 [head_dim] norm weight, 16-byte aligned.
+ * cos, sin     device pointers, bf16 [total_tokens, rotary_dim], one row per token (row t serves
+ *              token t of every head), 16-byte aligned; may be NULL when rotary_dim is 0.
+ * rotary_dim   R: a multiple of 16 in [0, 128] (96 for the H3 blocks), else LSV_ERR_UNSUPPORTED.
+ * eps          finite, >= 0 (1e-5 for the H3 blocks).
+ */
+int lsv_attn_fwd_qnorm(const void* q, const void* k, const void* v, const void* q_weight, const void* cos,
+                       const void* sin, int32_t rotary_dim, float eps, void* o, float* lse,
+                       const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens,
+                       int32_t n_heads, int32_t head_dim, float scale, void* stream);
+
 /* Workspace bytes lsv_attn_fwd_split needs for n_split key ranges: n_split partial rows of
  * head_dim + 1 fp32 values per (token, head), i.e. 4 * n_split * total_tokens * n_heads * 129;
  * 0 for n_split = 1. Returns -1 for a negative size, n_heads < 1 or n_split outside [1, 8]. */
@@ -91,6 +121,46 @@ int64_t lsv_attn_fwd_split_workspace_size(int64_t total_tokens, int32_t n_heads,
 int lsv_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
                        int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
                        float scale, int32_t n_split, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The key split that lsv_attn_fwd_tail applies for these sizes on compute_units workgroup slots
+ * (one workgroup of 256 query rows per compute unit, compute_units / 8 on each of the 8 XCDs).
+ * With n = ceil(max_seqlen / 256) * n_seqs * n_heads query tiles, each XCD owns n / 8 consecutive
+ * tiles, as in lsv_attn_fwd; the t = (n / 8) mod (compute_units / 8) of them past its last whole
+ * round are cut into *n_split key ranges when t is at most a quarter of a round -- as many ranges
+ * as fill the XCD's slots, at most 8, each of at least 1024 keys of a max_seqlen-key segment --
+ * and *n_tail_tiles = 8 t. Otherwise, and whenever n is not a multiple of 8, *n_split = 1 and
+ * *n_tail_tiles = 0 (nothing is cut). compute_units must be a positive multiple of 8 (256 on
+ * MI355X; lsv_device_peak reports it). Host-only arithmetic; LSV_ERR_INVALID_ARG on bad sizes. */
+int lsv_attn_fwd_tail_plan(int32_t n_seqs, int32_t max_seqlen, int32_t n_heads, int32_t compute_units,
+                           int32_t* n_split, int64_t* n_tail_tiles);
+
+/* Workspace bytes lsv_attn_fwd_tail may need: compute_units * 256 rows * 129 fp32 values (an
+ * upper bound for any sizes); -1 unless compute_units is a positive multiple of 8. */
+int64_t lsv_attn_fwd_tail_workspace_size(int32_t compute_units);
+
+/* Attention forward that fills the last, partial round of workgroups (asynchronous; one kernel,
+ * plus a small combine pass when it cuts tiles). The same operation as lsv_attn_fwd (the varlen
+ * forward of FastVideo #2049). The query tiles of the whole rounds run as in lsv_attn_fwd, on
+ * the same XCDs and in the same order; each XCD's tiles of its last, partial round are cut into
+ * key ranges (lsv_attn_fwd_tail_plan) that run after them on that XCD, and their partial
+ * softmaxes are merged as in lsv_attn_fwd_split:
+ *     LSE = ln sum_r exp(LSE_r),   O = sum_r exp(LSE_r - LSE) O_r   (fp32, then bf16 nearest even).
+ * A launch of n query tiles otherwise runs ceil(n / compute_units) rounds with the last one
+ * partly idle: 14 heads x 19,394 tokens is 1,064 tiles, 4.16 rounds of 256 compute units. Results differ from lsv_attn_fwd's by rounding only (the whole
+ * tiles are bit-identical to it) and are deterministic. When nothing is cut this is
+ * lsv_attn_fwd itself and the workspace is not used.
+ *
+ * q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+ * stream: as for lsv_attn_fwd (same layouts, limits and skipped-segment rule).
+ * compute_units  workgroup slots to plan for: a positive multiple of 8 (the device's compute-unit
+ *              count), else LSV_ERR_INVALID_ARG.
+ * workspace    device pointer, 16-byte aligned, at least n_tail_tiles * n_split * 256 * 129 * 4
+ *              bytes for the plan (lsv_attn_fwd_tail_workspace_size always suffices); overwritten.
+ *              Owned by the caller.
+ */
+int lsv_attn_fwd_tail(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                      int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                      float scale, int32_t compute_units, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* FP8 (e4m3) attention forward on the caller's stream (asynchronous).
  *
@@ -207,6 +277,24 @@ int64_t lsv_attn_bwd_noalloc_max_rows(void);
 int lsv_qkv_prologue(const void* q, const void* k, const void* v, const void* q_weight, const void* k_weight,
                      const void* cos, const void* sin, void* out, int64_t batch, int64_t seq_len, int32_t n_heads,
                      int32_t head_dim, int32_t rotary_dim, float eps, void* stream);
+
+/* The QKV prologue's per-row step on one tensor (asynchronous): every (token t, head) row x of
+ * x becomes y_i = x_i * rsqrt(mean_d x_d^2 + eps) * weight_i, rotated on its first R channels
+ * with the cos/sin row of token t (as lsv_attn_fwd_qnorm describes), in fp32, rounded once to
+ * bf16 (the MotionKernel qkv_prologue of FastVideo #2049; bit-identical to lsv_qkv_prologue's Q
+ * or K plane for one sequence). The K side of a forward whose Q side is lsv_attn_fwd_qnorm.
+ *
+ * x, out       device pointers, bf16 [total_tokens, n_heads, head_dim], 16-byte aligned, not
+ *              overlapping.
+ * weight       device pointer, bf16 [head_dim].
+ * cos, sin     device pointers, bf16 [total_tokens, rotary_dim], 16-byte aligned; may be NULL when
+ *              rotary_dim is 0.
+ * total_tokens >= 0 (0: successful no-op); total_tokens * n_heads < 2^31.
+ * n_heads >= 1; head_dim must be 128; rotary_dim a multiple of 16 in [0, 128]; eps finite, >= 0.
+ */
+int lsv_norm_rope(const void* x, const void* weight, const void* cos, const void* sin, void* out,
+                  int64_t total_tokens, int32_t n_heads, int32_t head_dim, int32_t rotary_dim, float eps,
+                  void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* lsv_status_string(int status);

@@ -6,10 +6,11 @@ Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in
 ``python -m long_sequence_video_amd.build``). The functions named like the C entry points
 (``lsv_attn_fwd``, ``lsv_attn_fwd_split``, ``lsv_attn_fwd_split_workspace_size``, ``lsv_attn_fwd_fp8``,
 ``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``, ``lsv_attn_bwd_noalloc``,
-``lsv_attn_bwd_noalloc_max_rows``, ``lsv_qkv_prologue``, ``lsv_status_string``,
-``lsv_device_peak``, ``lsv_tile_config``) only marshal arguments; ``attn_fwd``,
-``attn_fwd_split``, ``attn_fwd_fp8``, ``attn_bwd``, ``attn_bwd_noalloc`` and ``qkv_prologue``
-add torch-tensor conveniences (shape checks, output and workspace allocation, the current
+``lsv_attn_bwd_noalloc_max_rows``, ``lsv_qkv_prologue``, ``lsv_attn_fwd_qnorm``, ``lsv_norm_rope``,
+``lsv_attn_fwd_tail``, ``lsv_attn_fwd_tail_plan``, ``lsv_attn_fwd_tail_workspace_size``,
+``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only marshal arguments;
+``attn_fwd``, ``attn_fwd_split``, ``attn_fwd_tail``, ``attn_fwd_fp8``, ``attn_bwd``,
+``attn_bwd_noalloc``, ``qkv_prologue``, ``attn_fwd_qnorm`` and ``norm_rope`` add torch-tensor conveniences (shape checks, output and workspace allocation, the current
 stream). There is no fallback: if the library is missing or a call fails, an exception is
 raised.
 
@@ -29,7 +30,9 @@ import os
 __all__ = [
     "LIB_PATH", "LsvError", "load_library", "lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_workspace_size",
     "lsv_attn_fwd_fp8", "attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_attn_bwd_noalloc",
-    "lsv_attn_bwd_noalloc_max_rows", "attn_bwd_noalloc", "lsv_qkv_prologue",
+    "lsv_attn_bwd_noalloc_max_rows", "attn_bwd_noalloc", "lsv_qkv_prologue", "lsv_attn_fwd_qnorm", "lsv_norm_rope",
+    "attn_fwd_qnorm", "norm_rope", "lsv_attn_fwd_tail", "lsv_attn_fwd_tail_plan", "lsv_attn_fwd_tail_workspace_size",
+    "attn_fwd_tail",
     "lsv_status_string", "lsv_device_peak", "lsv_tile_config", "attn_fwd", "attn_fwd_split", "choose_split",
     "attn_bwd", "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
 ]
@@ -37,8 +40,9 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsv.so")
 EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_workspace_size", "lsv_attn_fwd_fp8",
                     "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_attn_bwd_noalloc",
-                    "lsv_attn_bwd_noalloc_max_rows", "lsv_qkv_prologue", "lsv_status_string", "lsv_device_peak",
-                    "lsv_tile_config")
+                    "lsv_attn_bwd_noalloc_max_rows", "lsv_qkv_prologue", "lsv_attn_fwd_qnorm", "lsv_norm_rope",
+                    "lsv_attn_fwd_tail", "lsv_attn_fwd_tail_plan", "lsv_attn_fwd_tail_workspace_size",
+                    "lsv_status_string", "lsv_device_peak", "lsv_tile_config")
 
 LSV_OK = 0
 LSV_ERR_INVALID_ARG = -1
@@ -98,6 +102,18 @@ def load_library(path: str = LIB_PATH):
     lib.lsv_attn_bwd_noalloc_max_rows.restype = i64
     lib.lsv_qkv_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_float, vp]
     lib.lsv_qkv_prologue.restype = ctypes.c_int
+    lib.lsv_attn_fwd_qnorm.argtypes = [vp] * 6 + [i32, ctypes.c_float, vp, vp, vp, i32, i32, i64, i32, i32,
+                                       ctypes.c_float, vp]
+    lib.lsv_attn_fwd_qnorm.restype = ctypes.c_int
+    lib.lsv_norm_rope.argtypes = [vp] * 5 + [i64, i32, i32, i32, ctypes.c_float, vp]
+    lib.lsv_norm_rope.restype = ctypes.c_int
+    lib.lsv_attn_fwd_tail.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, i32, vp, i64,
+                                      vp]
+    lib.lsv_attn_fwd_tail.restype = ctypes.c_int
+    lib.lsv_attn_fwd_tail_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.lsv_attn_fwd_tail_plan.restype = ctypes.c_int
+    lib.lsv_attn_fwd_tail_workspace_size.argtypes = [i32]
+    lib.lsv_attn_fwd_tail_workspace_size.restype = i64
     lib.lsv_status_string.argtypes = [ctypes.c_int]
     lib.lsv_status_string.restype = ctypes.c_char_p
     lib.lsv_device_peak.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
@@ -200,6 +216,43 @@ def lsv_qkv_prologue(q: int, k: int, v: int, q_weight: int, k_weight: int, cos: 
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().lsv_qkv_prologue(q, k, v, q_weight, k_weight, cos, sin, out, batch, seq_len, n_heads,
                                            head_dim, rotary_dim, eps, stream)
+
+
+def lsv_attn_fwd_qnorm(q: int, k: int, v: int, q_weight: int, cos: int, sin: int, rotary_dim: int, eps: float,
+                       o: int, lse: int, cu_seqlens: int, n_seqs: int, max_seqlen: int, total_tokens: int,
+                       n_heads: int, head_dim: int, scale: float, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_fwd_qnorm(q, k, v, q_weight, cos, sin, rotary_dim, eps, o, lse, cu_seqlens,
+                                             n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale, stream)
+
+
+def lsv_norm_rope(x: int, weight: int, cos: int, sin: int, out: int, total_tokens: int, n_heads: int,
+                  head_dim: int, rotary_dim: int, eps: float, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_norm_rope(x, weight, cos, sin, out, total_tokens, n_heads, head_dim, rotary_dim, eps,
+                                        stream)
+
+
+def lsv_attn_fwd_tail(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, n_seqs: int, max_seqlen: int,
+                      total_tokens: int, n_heads: int, head_dim: int, scale: float, compute_units: int, workspace: int,
+                      workspace_bytes: int, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_fwd_tail(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads,
+                                            head_dim, scale, compute_units, workspace, workspace_bytes, stream)
+
+
+def lsv_attn_fwd_tail_plan(n_seqs: int, max_seqlen: int, n_heads: int, compute_units: int) -> tuple[int, int]:
+    """(key ranges per tail tile, tail tiles) of lsv_attn_fwd_tail for these sizes."""
+    s, t = ctypes.c_int32(), ctypes.c_int64()
+    rc = load_library().lsv_attn_fwd_tail_plan(n_seqs, max_seqlen, n_heads, compute_units, ctypes.byref(s),
+                                               ctypes.byref(t))
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_fwd_tail_plan")
+    return s.value, t.value
+
+
+def lsv_attn_fwd_tail_workspace_size(compute_units: int) -> int:
+    return load_library().lsv_attn_fwd_tail_workspace_size(compute_units)
 
 
 def lsv_status_string(status: int) -> str:
@@ -343,6 +396,64 @@ def attn_fwd_split(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: fl
                                 s.cuda_stream)
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_attn_fwd_split")
+    return out, lse
+
+
+def attn_fwd_tail(q, k, v, cu_seqlens, max_seqlen: int | None = None, scale: float | None = None, *,
+                  compute_units: int | None = None, out=None, lse=None, workspace=None, stream=None):
+    """Attention forward that cuts the query tiles of the last, partial round of workgroups into
+    key ranges (``lsv_attn_fwd_tail``). Arguments as for ``attn_fwd``; ``compute_units`` defaults
+    to the device's count; ``workspace``, if given, is a contiguous device buffer of at least
+    ``lsv_attn_fwd_tail_workspace_size(compute_units)`` bytes (else one is allocated).
+    Returns ``(out, lse)``."""
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [total_tokens, heads, head_dim] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in (k, v, cu_seqlens)):
+        raise ValueError("all tensors must be on the same GPU")
+    total, heads, dim = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    if compute_units is None:
+        compute_units = lsv_device_peak(dev.index if dev.index is not None else torch.cuda.current_device())[1]
+    mine = []
+    if out is None:
+        out = torch.empty_like(q)
+        mine.append(out)
+    if lse is None:
+        lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+        mine.append(lse)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's GPU")
+    if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != dev:
+        raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor on q's GPU")
+    need = lsv_attn_fwd_tail_workspace_size(compute_units)
+    if need < 0:
+        raise ValueError("compute_units must be a positive multiple of 8")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        mine.append(workspace)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous buffer on the same GPU")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_fwd_tail(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, max_seqlen, total, heads, dim, scale,
+                               compute_units, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_fwd_tail")
     return out, lse
 
 
@@ -495,6 +606,116 @@ def attn_bwd_noalloc(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int | None
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_attn_bwd_noalloc")
     return dq, dk, dv
+
+
+def _tables(cos, sin, total, dev):
+    """(rotary width, cos, sin) after checking per-token bf16 tables [total, R] (or both None)."""
+    import torch
+    if (cos is None) != (sin is None):
+        raise ValueError("cos and sin must both be given or both be None")
+    if cos is None:
+        return 0, None, None
+    for t in (cos, sin):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.shape[0] != total or not t.is_contiguous() or t.device != dev:
+            raise ValueError("cos/sin must be contiguous bfloat16 [total_tokens, R] tables on the inputs' GPU")
+    if cos.shape != sin.shape:
+        raise ValueError("cos and sin must have one shape")
+    return int(cos.shape[1]), cos, sin
+
+
+def norm_rope(x, weight, cos=None, sin=None, *, eps: float = 1e-5, out=None, stream=None):
+    """The QKV prologue's per-row RMSNorm + partial rotate-half RoPE on one tensor (e.g. K).
+
+    Args:
+      x: bfloat16 ``[total_tokens, heads, 128]``, contiguous, one GPU.
+      weight: bfloat16 ``[128]``.
+      cos, sin: bfloat16 ``[total_tokens, R]`` per-token tables (R a multiple of 16), or None.
+      eps, out, stream: the epsilon, an optional preallocated output, the stream.
+
+    Returns:
+      the normalised, rotated tensor (bf16, shaped like x).
+    """
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("x must be a contiguous bfloat16 [total_tokens, heads, head_dim] GPU tensor")
+    dev = x.device
+    total, heads, dim = x.shape
+    if weight.dtype != torch.bfloat16 or weight.shape != (dim,) or not weight.is_contiguous() or weight.device != dev:
+        raise ValueError("weight must be a contiguous bfloat16 [head_dim] tensor on x's GPU")
+    rd, cos, sin = _tables(cos, sin, total, dev)
+    mine = []
+    if out is None:
+        out = torch.empty_like(x)
+        mine.append(out)
+    if out.shape != x.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like x")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
+    with torch.cuda.device(dev):
+        rc = lsv_norm_rope(x.data_ptr(), weight.data_ptr(), 0 if cos is None else cos.data_ptr(),
+                           0 if sin is None else sin.data_ptr(), out.data_ptr(), total, heads, dim, rd, eps,
+                           s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_norm_rope")
+    return out
+
+
+def attn_fwd_qnorm(q, k, v, q_weight, cos, sin, cu_seqlens, max_seqlen: int | None = None,
+                   scale: float | None = None, *, eps: float = 1e-5, out=None, lse=None, stream=None):
+    """Attention forward with Q's RMSNorm + partial RoPE applied in the kernel's Q-tile load.
+
+    Args:
+      q: bfloat16 raw queries ``[total_tokens, heads, 128]``; k (already normalised and
+        rotated, e.g. by ``norm_rope``) and v as for ``attn_fwd``.
+      q_weight: bfloat16 ``[128]``; cos, sin: bfloat16 ``[total_tokens, R]`` per-token tables,
+        or None (R = 0).
+      cu_seqlens, max_seqlen, scale, out, lse, stream: as for ``attn_fwd``; eps the RMSNorm epsilon.
+
+    Returns:
+      ``(out, lse)``, equal bit for bit to ``attn_fwd(norm_rope(q, q_weight, cos, sin), k, v, ...)``.
+    """
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [total_tokens, heads, head_dim] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in (k, v, cu_seqlens, q_weight)):
+        raise ValueError("all tensors must be on the same GPU")
+    total, heads, dim = q.shape
+    if q_weight.dtype != torch.bfloat16 or q_weight.shape != (dim,) or not q_weight.is_contiguous():
+        raise ValueError("q_weight must be a contiguous bfloat16 [head_dim] tensor")
+    rd, cos, sin = _tables(cos, sin, total, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    mine = []
+    if out is None:
+        out = torch.empty_like(q)
+        mine.append(out)
+    if lse is None:
+        lse = torch.empty((heads, total), dtype=torch.float32, device=dev)
+        mine.append(lse)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's GPU")
+    if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != dev:
+        raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor on q's GPU")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_fwd_qnorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_weight.data_ptr(),
+                                0 if cos is None else cos.data_ptr(), 0 if sin is None else sin.data_ptr(), rd, eps,
+                                out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                max_seqlen, total, heads, dim, scale, s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_fwd_qnorm")
+    return out, lse
 
 
 def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, cu_seqlens,

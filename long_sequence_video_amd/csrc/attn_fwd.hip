@@ -428,27 +428,125 @@ __device__ __forceinline__ int keys_per_split(int seg_len, int n_split) {
   return ((seg_len + n_split - 1) / n_split + kBK - 1) / kBK * kBK;
 }
 
+// The Q-side prologue of lsv_attn_fwd_qnorm: raw q rows are RMS-normalised with weight w and
+// rotated (rotate-half RoPE on the first R channels, one cos/sin table row per token) as the
+// Q tile is loaded.
+struct QNorm {
+  const uint16_t* w;    // bf16 [128]
+  const uint16_t* cos;  // bf16 [total_tokens, R]
+  const uint16_t* sin;
+  int r;                // rotary width R, a multiple of 16 in [0, 128]
+  float eps;
+};
+
+__device__ __forceinline__ void unpack8(const u32x4& u, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+
+// This lane's Q^T operand from the raw row at `qrow` (token `tok`): chunk s holds channels
+// 16 s + 8 h32 .. +7. The arithmetic is the standalone prologue's, step for step, so the operand
+// is bit-identical to what that pass would have written: per 8-channel chunk an fma chain of
+// squares; the 16 chunk sums of the row added in the same tree (chunk j = 2 s + h32 with
+// j ^ 8, j ^ 4, j ^ 2 -- the same lane -- then j ^ 1, the partner lane l ^ 32);
+// inv = rsq(ss / 128 + eps); y = x inv w; a rotated channel i is fma(y_p, -+sin_i, y_i cos_i)
+// with partner channel p = i +- R/2 (its raw chunk read again from the row); one rounding to bf16.
+__device__ __forceinline__ void load_q_normed(const char* qrow, int64_t tok, int h32, const QNorm& qn,
+                                              bf16x8 (&qr)[8]) {
+  float x[8][8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) unpack8(*(const u32x4*)(qrow + 32 * s + 16 * h32), x[s]);
+  float p[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = __builtin_fmaf(x[s][e], x[s][e], a);
+    p[s] = a;
+  }
+  float t1[4], t2[2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) t1[s] = p[s] + p[s + 4];
+  t2[0] = t1[0] + t1[2];
+  t2[1] = t1[1] + t1[3];
+  const float ss = pair_sum(t2[0] + t2[1]);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + qn.eps);
+  const int half = qn.r >> 1;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int i0 = 16 * s + 8 * h32;  // first channel of this chunk
+    float w[8];
+    unpack8(*(const u32x4*)(qn.w + i0), w);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = x[s][e] * inv * w[e];
+    if (i0 < qn.r) {
+      const int ip = i0 < half ? i0 + half : i0 - half;
+      const float sgn = i0 < half ? -1.0f : 1.0f;
+      float xp[8], wp[8], cs[8], sn[8];
+      unpack8(*(const u32x4*)(qrow + 2 * ip), xp);
+      unpack8(*(const u32x4*)(qn.w + ip), wp);
+      unpack8(*(const u32x4*)(qn.cos + tok * qn.r + i0), cs);
+      unpack8(*(const u32x4*)(qn.sin + tok * qn.r + i0), sn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float yp = xp[e] * inv * wp[e];
+        o[e] = __builtin_fmaf(yp, sgn * sn[e], o[e] * cs[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qr[s][e] = (__bf16)o[e];
+  }
+}
+
 // One workgroup: 256 query rows of one (segment, head) against all keys of the segment, or,
 // with kSplit, against key range `split` of n_split; then O (bf16) and LSE are written, or,
 // with kSplit, this range's normalised fp32 O and its LSE into the partial buffers.
-template <bool kSplit>
+//
+// With kTail (lsv_attn_fwd_tail; n_logical and n_tail multiples of 8): XCD x owns logical
+// tiles [x P, (x + 1) P), P = n_logical / 8, exactly as in the plain launch. Its first
+// P - n_tail / 8 tiles run whole, in the same order as there; its last n_tail / 8 tiles (its
+// last, partial round) are cut into n_split key ranges and run after them, on the same XCD.
+// Tail tile i = x * (n_tail / 8) + r and range s form piece s * n_tail + i, which writes its
+// range's fp32 O and LSE to row (piece * 256 + row in tile) of the partial buffers.
+template <bool kSplit, bool kQNorm = false, bool kTail = false>
 __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                                          float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens, int n_seqs,
                                          int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens,
                                          float c, int n_logical, int n_split, float* __restrict__ part_o,
-                                         float* __restrict__ part_lse) {
+                                         float* __restrict__ part_lse, QNorm qn = QNorm{}, int n_tail = 0) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
 
   // XCD-aware order: hardware dispatches block b to XCD b % 8; give each XCD a contiguous
   // range of logical tiles (head-major, then segment in packed order, then key range, then
   // query tile).
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (logical >= n_logical) return;
+  int logical, split = 0, piece = -1;
+  if (kTail) {
+    const int xcd = blockIdx.x & 7;
+    const int j = blockIdx.x >> 3;  // this block's place in its XCD's sequence
+    const int per_xcd = n_logical >> 3;
+    const int t = n_tail >> 3;
+    if (j < per_xcd - t) {
+      logical = xcd * per_xcd + j;
+    } else {
+      const int jt = j - (per_xcd - t);
+      if (jt >= t * n_split) return;
+      split = jt / t;
+      const int r = jt - split * t;
+      logical = xcd * per_xcd + per_xcd - t + r;
+      piece = split * n_tail + xcd * t + r;
+    }
+  } else {
+    const int per_xcd = gridDim.x >> 3;
+    logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (logical >= n_logical) return;
+  }
   const int qt = logical % tiles_per_seq;
   int hs = logical / tiles_per_seq;
-  int split = 0;
   if (kSplit) {
     split = hs % n_split;
     hs /= n_split;
@@ -463,7 +561,7 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
   const int q0 = qt * kBQ;
   if (q0 >= seg_len) return;
   int k0 = 0, k_len = seg_len;  // this workgroup's keys: [k0, k0 + k_len) of the segment
-  if (kSplit) {
+  if (kSplit || (kTail && piece >= 0)) {
     const int per = keys_per_split(seg_len, n_split);
     k0 = split * per;
     k_len = min(per, seg_len - k0);
@@ -497,14 +595,19 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
   for (int s = 0; s < 8; ++s) ln.kaddr[s] = row_read_addr(lds_base, ln.l32, ln.h32, s);
   ln.vaddr = tr_read_base(lds_base + kRingBytes, ln.lane);
 
-  // Q^T operand: lane holds q[row][16 s + 8 h32 .. +7] for s = 0..7.
+  // Q^T operand: lane holds q[row][16 s + 8 h32 .. +7] for s = 0..7 (normalised and rotated
+  // on the way in for lsv_attn_fwd_qnorm).
   bf16x8 qr[8];
   {
     int row = q0 + wave * kWaveQ + ln.l32;
     row = row < seg_len ? row : seg_len - 1;
-    const char* qrow = (const char*)q + ((int64_t)(seg_start + row) * n_heads + head) * kRowBytes + ln.h32 * 16;
+    const char* qrow = (const char*)q + ((int64_t)(seg_start + row) * n_heads + head) * kRowBytes;
+    if (kQNorm) {
+      load_q_normed(qrow, (int64_t)seg_start + row, ln.h32, qn, qr);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qr[s] = *(const bf16x8*)(qrow + s * 32);
+      for (int s = 0; s < 8; ++s) qr[s] = *(const bf16x8*)(qrow + ln.h32 * 16 + s * 32);
+    }
   }
 
   Acc acc;
@@ -535,8 +638,10 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
   if (row < seg_len) {
     const int64_t tok = (int64_t)seg_start + row;
     const float lse_row = (acc.m * c + __log2f(l)) * 0.69314718055994530942f;
-    if (kSplit) {
-      float* prow = part_o + (((int64_t)split * total_tokens + tok) * n_heads + head) * kD;
+    if (kSplit || (kTail && piece >= 0)) {
+      const int64_t prow_idx = kTail ? (int64_t)piece * kBQ + (row - q0)
+                                     : ((int64_t)split * total_tokens + tok) * n_heads + head;
+      float* prow = part_o + prow_idx * kD;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -546,7 +651,8 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
           for (int e = 0; e < 4; ++e) w[e] = acc.O[db][4 * g + e] / lb;
           *(f32x4*)(prow + 32 * db + 8 * g + 4 * ln.h32) = w;
         }
-      if (ln.h32 == 0) part_lse[((int64_t)split * n_heads + head) * total_tokens + tok] = lse_row;
+      if (ln.h32 == 0)
+        part_lse[kTail ? prow_idx : ((int64_t)split * n_heads + head) * total_tokens + tok] = lse_row;
     } else {
       uint16_t* orow = o + (tok * n_heads + head) * kD;
 #pragma unroll
@@ -578,12 +684,94 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_qnorm_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                      uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                      int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
+                      int n_logical, QNorm qn) {
+  fwd_body<false, true>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c,
+                        n_logical, 1, nullptr, nullptr, qn);
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, int n_seqs,
                       int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c, int n_logical,
                       int n_split, float* __restrict__ part_o, float* __restrict__ part_lse) {
   fwd_body<true>(q, k, v, nullptr, nullptr, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c,
                  n_logical, n_split, part_o, part_lse);
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_tail_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                     uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                     int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
+                     int n_logical, int n_tail, int n_split, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  fwd_body<false, false, true>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens,
+                               c, n_logical, n_split, part_o, part_lse, QNorm{}, n_tail);
+}
+
+// Combines the key ranges of the tail tiles of attn_fwd_tail_kernel: block i takes tail tile
+// i = x * (n_tail / 8) + r, the logical tile x P + P - n_tail / 8 + r (P = n_logical / 8), and
+// merges its rows' ranges as attn_fwd_combine_kernel does (the same segment checks; empty
+// ranges left out; fp32, then bf16 nearest even).
+__global__ void __launch_bounds__(256)
+attn_fwd_tail_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                             uint16_t* __restrict__ o, float* __restrict__ lse,
+                             const int32_t* __restrict__ cu_seqlens, int n_seqs, int tiles_per_seq, int max_seqlen,
+                             int n_heads, int64_t total_tokens, int n_logical, int n_tail, int n_split) {
+  const int t = blockIdx.x;
+  if (t >= n_tail) return;
+  const int per_xcd = n_logical >> 3;
+  const int tail_per_xcd = n_tail >> 3;
+  const int logical = (t / tail_per_xcd + 1) * per_xcd - tail_per_xcd + t % tail_per_xcd;
+  const int qt = logical % tiles_per_seq;
+  const int hs = logical / tiles_per_seq;
+  const int seg = hs % n_seqs;
+  const int head = hs / n_seqs;
+  const int seg_start = cu_seqlens[seg];
+  const int seg_end = cu_seqlens[seg + 1];
+  if (seg_start < 0 || seg_end < seg_start || (int64_t)seg_end > total_tokens) return;
+  const int seg_len = seg_end - seg_start;
+  if (seg_len > max_seqlen) return;
+  const int q0 = qt * kBQ;
+  if (q0 >= seg_len) return;
+  const int per = keys_per_split(seg_len, n_split);
+  const int n_ranges = (seg_len + per - 1) / per;
+  const int j = threadIdx.x & 15;
+  const int q_end = min(q0 + kBQ, seg_len);
+  for (int row = q0 + (threadIdx.x >> 4); row < q_end; row += 16) {
+    const int64_t tok = (int64_t)seg_start + row;
+    float m = -INFINITY;
+    for (int r = 0; r < n_ranges; ++r) m = fmaxf(m, part_lse[(int64_t)(r * n_tail + t) * kBQ + (row - q0)]);
+    float sum = 0.f;
+    f32x4 a = {}, b = {};
+    for (int r = 0; r < n_ranges; ++r) {
+      const int64_t pr = (int64_t)(r * n_tail + t) * kBQ + (row - q0);
+      const float w = __expf(part_lse[pr] - m);
+      sum += w;
+      const f32x4* src = (const f32x4*)(part_o + pr * kD + 8 * j);
+      const f32x4 x = src[0], y = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = __builtin_fmaf(w, x[e], a[e]);
+        b[e] = __builtin_fmaf(w, y[e], b[e]);
+      }
+    }
+    const float inv = 1.f / sum;
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      bf16x2 lo, hi;
+      lo[0] = (__bf16)(a[2 * e] * inv);
+      lo[1] = (__bf16)(a[2 * e + 1] * inv);
+      hi[0] = (__bf16)(b[2 * e] * inv);
+      hi[1] = (__bf16)(b[2 * e + 1] * inv);
+      pk[e] = __builtin_bit_cast(unsigned, lo);
+      pk[2 + e] = __builtin_bit_cast(unsigned, hi);
+    }
+    *(u32x4*)(o + (tok * n_heads + head) * kD + 8 * j) = pk;
+    if (j == 0) lse[(int64_t)head * total_tokens + tok] = m + __logf(sum);
+  }
 }
 
 // Combines the key ranges of attn_fwd_split_kernel: per (token, head) row, with LSE_s of the
@@ -648,6 +836,31 @@ attn_fwd_combine_kernel(const float* __restrict__ part_o, const float* __restric
 
 constexpr int kProceed = 1;  // fwd_checks: arguments valid and there is work to launch
 constexpr int kMaxSplit = 8;
+constexpr int kMinTailKeys = 1024;  // a tail tile's key ranges keep at least this many keys
+
+// The tail split of lsv_attn_fwd_tail for n_logical query tiles on `units` workgroup slots
+// (units / 8 per XCD). Each XCD owns n_logical / 8 consecutive tiles, as in the plain launch;
+// the t of them past its last whole round are cut into key ranges when t is at most a quarter
+// of a round, into as many ranges as fill the XCD's slots (at most kMaxSplit, and each of at
+// least kMinTailKeys keys of a max_seqlen-key segment). n_tail = 8 t. Nothing is cut (n_split
+// = 1, n_tail = 0) when n_logical is not a multiple of 8. (Measured on MI355X: a round half
+// full costs less than a full one -- the idle half lets the busy half clock higher -- and
+// cutting it into 2 ranges gained nothing at 4,096 x 56; a round one-sixth full, at 19,394 x
+// 14, cut into 6 ranges gained 9%.)
+void tail_plan(int64_t n_logical, int32_t max_seqlen, int32_t units, int32_t* n_split, int64_t* n_tail) {
+  *n_split = 1;
+  *n_tail = 0;
+  if (n_logical % 8 != 0) return;
+  const int64_t slots = units / 8;
+  const int64_t t = (n_logical / 8) % slots;
+  if (t == 0 || t > slots / 4) return;
+  int64_t split = slots / t;
+  if (split > kMaxSplit) split = kMaxSplit;
+  if (split > max_seqlen / kMinTailKeys) split = max_seqlen / kMinTailKeys;
+  if (split < 2) return;
+  *n_split = (int32_t)split;
+  *n_tail = 8 * t;
+}
 
 // The forward's argument checks (before any HIP call): a status to return, or kProceed with the
 // number of 256-row query tiles per segment.
@@ -722,6 +935,94 @@ int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens,
                      (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical);
+  if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
+  return LSV_OK;
+}
+
+int lsv_attn_fwd_qnorm(const void* q, const void* k, const void* v, const void* q_weight, const void* cos,
+                       const void* sin, int32_t rotary_dim, float eps, void* o, float* lse,
+                       const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens,
+                       int32_t n_heads, int32_t head_dim, float scale, void* stream) {
+  if (!(eps >= 0.f) || !isfinite(eps)) return LSV_ERR_INVALID_ARG;
+  if (rotary_dim < 0 || rotary_dim > kD || rotary_dim % 16 != 0) return LSV_ERR_UNSUPPORTED;
+  int64_t tiles = 0;
+  const int rc = fwd_checks(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                            &tiles);
+  if (rc != kProceed) return rc;
+  if (!q_weight || (rotary_dim > 0 && (!cos || !sin))) return LSV_ERR_INVALID_ARG;
+  if (((uintptr_t)q_weight | (uintptr_t)cos | (uintptr_t)sin) & 15) return LSV_ERR_ALIGNMENT;
+  const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
+  const int64_t grid = (n_logical + 7) / 8 * 8;
+  if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute((const void*)attn_fwd_qnorm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return LSV_ERR_HIP;
+  QNorm qn;
+  qn.w = (const uint16_t*)q_weight;
+  qn.cos = (const uint16_t*)cos;
+  qn.sin = (const uint16_t*)sin;
+  qn.r = rotary_dim;
+  qn.eps = eps;
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attn_fwd_qnorm_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens,
+                     (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical, qn);
+  if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
+  return LSV_OK;
+}
+
+int lsv_attn_fwd_tail_plan(int32_t n_seqs, int32_t max_seqlen, int32_t n_heads, int32_t compute_units,
+                           int32_t* n_split, int64_t* n_tail_tiles) {
+  if (n_seqs < 0 || max_seqlen < 0 || n_heads < 1 || compute_units < 8 || compute_units % 8 != 0 || !n_split ||
+      !n_tail_tiles)
+    return LSV_ERR_INVALID_ARG;
+  const int64_t tiles = ((int64_t)max_seqlen + kBQ - 1) / kBQ;
+  tail_plan(tiles * n_seqs * (int64_t)n_heads, max_seqlen, compute_units, n_split, n_tail_tiles);
+  return LSV_OK;
+}
+
+int64_t lsv_attn_fwd_tail_workspace_size(int32_t compute_units) {
+  if (compute_units < 8 || compute_units % 8 != 0) return -1;
+  return (int64_t)compute_units * kBQ * (kD + 1) * (int64_t)sizeof(float);
+}
+
+int lsv_attn_fwd_tail(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                      int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                      float scale, int32_t compute_units, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (compute_units < 8 || compute_units % 8 != 0) return LSV_ERR_INVALID_ARG;
+  int64_t tiles = 0;
+  const int rc = fwd_checks(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                            &tiles);
+  if (rc != kProceed) return rc;
+  const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
+  int32_t n_split = 1;
+  int64_t n_tail = 0;
+  tail_plan(n_logical, max_seqlen, compute_units, &n_split, &n_tail);
+  if (n_split == 1)
+    return lsv_attn_fwd(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                        stream);
+  if (!workspace) return LSV_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 15) return LSV_ERR_ALIGNMENT;
+  const int64_t pieces = n_tail * n_split;
+  if (workspace_bytes < pieces * kBQ * (kD + 1) * (int64_t)sizeof(float)) return LSV_ERR_INVALID_ARG;
+  const int64_t grid = n_logical - n_tail + pieces;  // a multiple of 8: the plan cuts only then
+  if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute((const void*)attn_fwd_tail_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return LSV_ERR_HIP;
+  float* part_o = (float*)workspace;
+  float* part_lse = part_o + pieces * kBQ * kD;
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  const hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attn_fwd_tail_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens, (int)n_seqs, (int)tiles,
+                     (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical, (int)n_tail, (int)n_split,
+                     part_o, part_lse);
+  hipLaunchKernelGGL(attn_fwd_tail_combine_kernel, dim3((unsigned)n_tail), dim3(256), 0, st, part_o, part_lse,
+                     (uint16_t*)o, lse, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads,
+                     total_tokens, (int)n_logical, (int)n_tail, (int)n_split);
   if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
   return LSV_OK;
 }

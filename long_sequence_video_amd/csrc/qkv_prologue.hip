@@ -162,7 +162,67 @@ qkv_prologue_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ k, co
   }
 }
 
+// The same per-row step on one tensor: x [rows, 128] -> out, with one cos/sin table row per
+// token (row / n_heads) -- the K side of a forward whose Q side is normalised in the attention
+// kernel's Q load (lsv_attn_fwd_qnorm).
+__global__ void __launch_bounds__(kThreads)
+norm_rope_kernel(const u32x4* __restrict__ x, const uint16_t* __restrict__ w, const u32x4* __restrict__ cosb,
+                 const u32x4* __restrict__ sinb, u32x4* __restrict__ out, unsigned n_rows, unsigned n_heads,
+                 int rotary_dim, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & (kLanesPerRow - 1);
+  const int h16 = rotary_dim / 16;
+  LaneConst lc;
+  lc.rotates = j < 2 * h16;
+  lc.sgn = j < h16 ? -1.0f : 1.0f;
+  const int jp = !lc.rotates ? j : (j < h16 ? j + h16 : j - h16);
+  lc.partner = (lane & ~(kLanesPerRow - 1)) | jp;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lc.wq[e] = __uint_as_float((unsigned)w[8 * j + e] << 16);
+    lc.wqp[e] = __uint_as_float((unsigned)w[8 * jp + e] << 16);
+  }
+  const int rvec = rotary_dim / 8;
+  const unsigned stride = gridDim.x * kRowsPerBlock;
+  const unsigned first = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  for (unsigned row = first; row < n_rows; row += stride) {
+    const int64_t idx = (int64_t)row * (kD / 8) + j;
+    const u32x4 xr = x[idx];
+    u32x4 cr = {}, sr = {};
+    if (lc.rotates) {
+      const unsigned tok = row / n_heads;
+      cr = cosb[(int64_t)tok * rvec + j];
+      sr = sinb[(int64_t)tok * rvec + j];
+    }
+    __builtin_nontemporal_store(norm_rope(xr, lc.wq, lc.wqp, lc, cr, sr, eps), out + idx);
+  }
+}
+
 }  // namespace
+
+extern "C" int lsv_norm_rope(const void* x, const void* weight, const void* cos, const void* sin, void* out,
+                             int64_t total_tokens, int32_t n_heads, int32_t head_dim, int32_t rotary_dim, float eps,
+                             void* stream) {
+  if (total_tokens < 0 || n_heads < 1) return LSV_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return LSV_ERR_INVALID_ARG;
+  if (head_dim != kD) return LSV_ERR_UNSUPPORTED;
+  if (rotary_dim < 0 || rotary_dim > kD || rotary_dim % 16 != 0) return LSV_ERR_UNSUPPORTED;
+  if (total_tokens == 0) return LSV_OK;
+  if (!x || !weight || !out) return LSV_ERR_INVALID_ARG;
+  if (rotary_dim > 0 && (!cos || !sin)) return LSV_ERR_INVALID_ARG;
+  if (((uintptr_t)x | (uintptr_t)out | (uintptr_t)cos | (uintptr_t)sin) & 15) return LSV_ERR_ALIGNMENT;
+  if ((uintptr_t)weight & 1) return LSV_ERR_ALIGNMENT;
+  const int64_t rows = total_tokens * (int64_t)n_heads;
+  if (total_tokens >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)) return LSV_ERR_UNSUPPORTED;
+  const int64_t need = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t grid = need < kMaxGrid ? need : kMaxGrid;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, (const u32x4*)x,
+                     (const uint16_t*)weight, (const u32x4*)cos, (const u32x4*)sin, (u32x4*)out, (unsigned)rows,
+                     (unsigned)n_heads, (int)rotary_dim, eps);
+  if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
+  return LSV_OK;
+}
 
 extern "C" int lsv_qkv_prologue(const void* q, const void* k, const void* v, const void* q_weight,
                                 const void* k_weight, const void* cos, const void* sin, void* out, int64_t batch,

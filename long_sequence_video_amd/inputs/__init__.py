@@ -165,7 +165,7 @@ class Inputs:
 
 def generate(seqlens, heads: int, head_dim: int = 128, *, seed: int, rms_qk: bool = False,
              k_boost_frac: float = 0.0, k_boost_factor: float = 8.0, scale: float | None = None,
-             name: str = "custom", total_tokens: int | None = None) -> Inputs:
+             low_first_tile: float = 0.0, name: str = "custom", total_tokens: int | None = None) -> Inputs:
     """Packed inputs for segments of lengths ``seqlens``.
 
     * q, k, v: iid N(0,1) rounded to bf16, streams (seed, 0/1/2), row-major
@@ -174,6 +174,11 @@ def generate(seqlens, heads: int, head_dim: int = 128, *, seed: int, rms_qk: boo
       weight, eps 1e-5) in double and rounded to bf16.
     * ``k_boost_frac``: ``round(frac * total)`` token rows of k, chosen by the
       (seed, 3) stream, are multiplied by ``k_boost_factor`` on every head.
+    * ``low_first_tile`` = c > 0: channel 0 of every q row is set to 8 and channel 0 of every
+      k row to +c, except the first 256 keys of each segment, which get -c (bf16 exact for
+      the values used). Every query then scores about 16 c * scale below the rest on its
+      segment's first key tile: the input on which a softmax that fixes its reference at the
+      first tile's maximum must fall back everywhere.
     * ``scale`` defaults to ``1/sqrt(head_dim)``.
     * ``total_tokens`` may exceed ``sum(seqlens)``; the extra rows are generated
       too but lie outside every segment.
@@ -202,6 +207,13 @@ def generate(seqlens, heads: int, head_dim: int = 128, *, seed: int, rms_qk: boo
         meta["k_boost_row_ids"] = rows
     cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(seqlens)
+    if low_first_tile > 0:
+        lift = f64_to_bf16_bits(np.array([low_first_tile, -low_first_tile, 8.0]))
+        q[:, :, 0] = lift[2]
+        k[:, :, 0] = lift[0]
+        for a, b in zip(cu[:-1], cu[1:]):
+            k[a:min(b, a + 256), :, 0] = lift[1]
+        meta["low_first_tile"] = float(low_first_tile)
     sc = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
     return Inputs(name, q, k, v, cu, sc, meta)
 
@@ -242,6 +254,79 @@ def rope_tables(seq_len: int, rotary_dim: int, *, base: float = 10000.0, start: 
     ang = (start + np.arange(seq_len, dtype=np.float64))[:, None] * inv_freq[None, :]
     ang = np.concatenate([ang, ang], axis=1)
     return f64_to_bf16_bits(np.cos(ang)), f64_to_bf16_bits(np.sin(ang))
+
+
+def rope_tables_varlen(seqlens, rotary_dim: int, *, base: float = 10000.0):
+    """Per-token cos/sin tables ``[sum(seqlens), R]`` (bf16 bits) for a varlen pack: each
+    segment's tokens take the positions 0, 1, ... of their own sequence."""
+    cs, ss = [], []
+    for n in seqlens:
+        c, s = rope_tables(int(n), rotary_dim, base=base)
+        cs.append(c)
+        ss.append(s)
+    if not cs:
+        return np.zeros((0, rotary_dim), np.uint16), np.zeros((0, rotary_dim), np.uint16)
+    return np.concatenate(cs), np.concatenate(ss)
+
+
+@dataclass
+class QNormInputs:
+    """A forward with the QKV prologue in front of it: raw q, k, v [T, H, 128], bf16 norm weights
+    [128] and per-token cos/sin tables [T, R] (bf16 bits), and the segment boundaries."""
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_weight: np.ndarray
+    k_weight: np.ndarray
+    cos: np.ndarray
+    sin: np.ndarray
+    cu_seqlens: np.ndarray
+    scale: float
+    eps: float = RMS_EPS
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def n_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def rotary_dim(self) -> int:
+        return int(self.cos.shape[1])
+
+    @property
+    def seqlens(self) -> list[int]:
+        cu = self.cu_seqlens.astype(np.int64)
+        return [int(b - a) for a, b in zip(cu[:-1], cu[1:])]
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.seqlens, default=0)
+
+    def flops(self) -> float:
+        return float(sum(4.0 * s * s * self.n_heads * self.q.shape[2] for s in self.seqlens))
+
+
+def generate_qnorm(seqlens, heads: int, rotary_dim: int = 96, *, seed: int, tables: str = "rope",
+                   name: str = "qnorm") -> QNormInputs:
+    """Raw q, k, v iid N(0,1) (streams (seed, 0/1/2)), norm weights iid N(0,1) (streams 4, 5) and
+    per-token tables: RoPE angles of each token's position in its segment (``"rope"``) or iid
+    N(0,1) (``"normal"``, streams 6, 7), for a varlen pack of ``seqlens``."""
+    inp = generate(seqlens, heads, seed=seed, name=name)
+    qw = normal_bf16(128, seed, QW_ID)
+    kw = normal_bf16(128, seed, KW_ID)
+    t = inp.total_tokens
+    if tables == "rope":
+        cos, sin = rope_tables_varlen(inp.seqlens, rotary_dim)
+    elif tables == "normal":
+        cos = normal_bf16(t * rotary_dim, seed, COS_ID).reshape(t, rotary_dim)
+        sin = normal_bf16(t * rotary_dim, seed, SIN_ID).reshape(t, rotary_dim)
+    else:
+        raise ValueError("tables must be 'rope' or 'normal'")
+    return QNormInputs(name, inp.q, inp.k, inp.v, qw, kw, cos, sin, inp.cu_seqlens, inp.scale)
 
 
 @dataclass

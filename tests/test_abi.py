@@ -293,3 +293,95 @@ def test_choose_split():
     assert lsv.choose_split([38000], 56) == 1
     assert lsv.choose_split([], 4) == 1 and lsv.choose_split([0, 0], 4) == 1
     assert lsv.choose_split([19394], 14, min_range_keys=1024) == 4   # fullest rounds: 16.6 of 17
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(rotary_dim=8), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(rotary_dim=144), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(rotary_dim=-16), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(scale=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(q=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(w=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(cos=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(w=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(sin=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(o=A + 2), lsv.LSV_ERR_ALIGNMENT),
+    (dict(max_seqlen=299_594, total_tokens=299_594, n_heads=56), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(n_seqs=0), lsv.LSV_OK),
+    (dict(rotary_dim=0, cos=0, sin=0, n_seqs=0), lsv.LSV_OK),
+])
+def test_attn_fwd_qnorm_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, w=A, cos=A, sin=A, rotary_dim=96, eps=1e-5, o=A, lse=A, cu=A, n_seqs=1, max_seqlen=10,
+             total_tokens=10, n_heads=4, head_dim=128, scale=0.125)
+    a.update(args)
+    rc = lsv.lsv_attn_fwd_qnorm(a["q"], a["k"], a["v"], a["w"], a["cos"], a["sin"], a["rotary_dim"], a["eps"], a["o"],
+                                a["lse"], a["cu"], a["n_seqs"], a["max_seqlen"], a["total_tokens"], a["n_heads"],
+                                a["head_dim"], a["scale"], None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(rotary_dim=24), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(eps=float("inf")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_heads=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(total_tokens=-1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(x=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(w=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(sin=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(out=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(w=A + 1), lsv.LSV_ERR_ALIGNMENT),
+    (dict(total_tokens=1 << 31), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(total_tokens=40_000_000, n_heads=56), lsv.LSV_ERR_UNSUPPORTED),   # rows >= 2^31
+    (dict(total_tokens=0), lsv.LSV_OK),
+    (dict(rotary_dim=0, cos=0, sin=0, total_tokens=0), lsv.LSV_OK),
+])
+def test_norm_rope_validation_before_any_hip_call(args, code):
+    a = dict(x=A, w=A, cos=A, sin=A, out=A, total_tokens=10, n_heads=4, head_dim=128, rotary_dim=96, eps=1e-5)
+    a.update(args)
+    rc = lsv.lsv_norm_rope(a["x"], a["w"], a["cos"], a["sin"], a["out"], a["total_tokens"], a["n_heads"],
+                           a["head_dim"], a["rotary_dim"], a["eps"], None)
+    assert rc == code
+
+
+def test_tail_plans():
+    """lsv_attn_fwd_tail's plans (host arithmetic): per XCD, n / 8 tiles, the ones past its last
+    whole round of compute_units / 8 cut when they are at most a quarter of it."""
+    assert lsv.lsv_attn_fwd_tail_plan(1, 19394, 14, 256) == (6, 40)      # 1,064 tiles: 133 per XCD, 5 past
+    assert lsv.lsv_attn_fwd_tail_plan(3, 104000, 56, 256) == (8, 24)     # the 161,394-token pack: 3 past
+    assert lsv.lsv_attn_fwd_tail_plan(1, 104000, 56, 256) == (8, 8)      # 2,849 per XCD: 1 past
+    assert lsv.lsv_attn_fwd_tail_plan(1, 4096, 56, 256) == (1, 0)        # 112 per XCD: half a round left whole
+    assert lsv.lsv_attn_fwd_tail_plan(1, 38000, 56, 256) == (1, 0)       # 1,043 per XCD: 19 past, over a quarter
+    assert lsv.lsv_attn_fwd_tail_plan(1, 256, 4, 256) == (1, 0)          # 4 tiles: not a multiple of 8
+    assert lsv.lsv_attn_fwd_tail_plan(1, 5000, 1, 16) == (1, 0)          # 20 tiles: not a multiple of 8
+    assert lsv.lsv_attn_fwd_tail_plan(1, 1024, 8, 256) == (1, 0)         # ranges would be under 1,024 keys
+    assert lsv.lsv_attn_fwd_tail_plan(2, 5000, 1, 256) == (4, 40)        # every tile cut: 5 per XCD of 32 slots
+    assert lsv.lsv_attn_fwd_tail_plan(2, 9000, 4, 256) == (8, 32)
+    with pytest.raises(lsv.LsvError):
+        lsv.lsv_attn_fwd_tail_plan(1, 4096, 56, 100)                    # not a multiple of 8
+    assert lsv.lsv_attn_fwd_tail_workspace_size(256) == 256 * 256 * 129 * 4
+    assert lsv.lsv_attn_fwd_tail_workspace_size(12) == -1
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(units=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(units=100), lsv.LSV_ERR_INVALID_ARG),
+    (dict(ws=0), lsv.LSV_ERR_INVALID_ARG),             # this plan cuts 6 ranges: a workspace is needed
+    (dict(ws=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(ws_bytes=40 * 6 * 256 * 129 * 4 - 1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(q=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(n_seqs=0, ws=0), lsv.LSV_OK),
+])
+def test_tail_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, n_seqs=1, max_seqlen=19394, total_tokens=19394, n_heads=14,
+             head_dim=128, scale=0.125, units=256, ws=A, ws_bytes=40 * 6 * 256 * 129 * 4)
+    a.update(args)
+    rc = lsv.lsv_attn_fwd_tail(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["n_seqs"], a["max_seqlen"],
+                               a["total_tokens"], a["n_heads"], a["head_dim"], a["scale"], a["units"], a["ws"],
+                               a["ws_bytes"], None)
+    assert rc == code

@@ -364,6 +364,22 @@ def test_very_negative_first_tile(gpu):
     compare(inp, out, lse, label="negfirst")
 
 
+def test_every_workgroup_on_exact_path_s38000_h56(gpu):
+    """38,000 x 56 with every query's first key tile ~113 nats (163 log2 units) below the rest
+    (channel 0: q = 8, k = -80 on the first 256 keys and +80 after): every workgroup's
+    fixed-reference pass overflows and the whole launch reruns on the exact path. Sampled rows
+    (first and last tiles included) against the oracle; the timed workload of the same name."""
+    import torch
+    inp = gen.generate([38000], 56, seed=1004, rms_qk=True, low_first_tile=80.0, name="fallback_s38000_h56")
+    c = float(np.float32(inp.scale)) * np.log2(np.e)
+    assert 2 * 8 * 80 * c > 160
+    say("case fallback_s38000_h56 (every workgroup exact)")
+    out, lse = run_kernel(inp, gpu)
+    compare(inp, out, lse, rows=sample_rows(inp, 48, seed=9, tile=32), label="fallback_s38000_h56")
+    del inp, out, lse
+    torch.cuda.empty_cache()
+
+
 def test_large_but_finite_growth_stays_on_fast_path(gpu):
     """Later keys score up to ~40 log2 units above the first tile (p up to ~2^40, no
     overflow): the fixed-reference path must still match the oracle."""

@@ -7,6 +7,10 @@ import pytest
 
 from long_sequence_video_amd import inputs as gen
 
+
+def bf16_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
 MASK = (1 << 64) - 1
 GAMMA = 0x9E3779B97F4A7C15
 
@@ -137,6 +141,21 @@ def test_generate_arguments():
     assert x.max_seqlen == 4 and x.seqlens == [3, 0, 4]
 
 
+def test_low_first_tile_sets_channel_zero_only():
+    """Channel 0: q = 8 everywhere, k = -c on each segment's first 256 keys and +c elsewhere
+    (also past cu[-1]); every other channel equals the plain draw."""
+    plain = gen.generate([300, 0, 40, 600], heads=2, seed=5, total_tokens=950)
+    low = gen.generate([300, 0, 40, 600], heads=2, seed=5, total_tokens=950, low_first_tile=80.0)
+    assert np.array_equal(low.q[:, :, 1:], plain.q[:, :, 1:]) and np.array_equal(low.v, plain.v)
+    assert np.array_equal(low.k[:, :, 1:], plain.k[:, :, 1:])
+    assert np.all(bf16_to_f64(low.q[:, :, 0]) == 8.0)
+    k0 = bf16_to_f64(low.k[:, :, 0])
+    first = np.zeros(950, bool)
+    first[0:256] = first[300:340] = first[340:596] = True
+    assert np.all(k0[first] == -80.0) and np.all(k0[~first] == 80.0)
+    assert low.meta["low_first_tile"] == 80.0
+
+
 def test_c_e4m3_quantiser_equals_the_numpy_definition():
     """The C quantiser (used for the FP8 workloads) gives the same bytes as
     ``f64_to_e4m3_bits(x / descale)`` on random values and on the edge cases: zeros of both
@@ -159,3 +178,16 @@ def test_c_amax_equals_numpy():
     vals = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert gen.amax_bf16(x) == np.abs(vals).max()
     assert gen.amax_bf16(np.zeros(0, np.uint16)) == 0.0
+
+
+def test_varlen_rope_tables_restart_per_segment():
+    """Each segment's tokens take positions 0, 1, ... of their own sequence: the first token of
+    every segment has cos 1 and sin 0, and a segment's rows equal the single-sequence table."""
+    seqlens = [5, 0, 9, 3]
+    cos, sin = gen.rope_tables_varlen(seqlens, 32)
+    assert cos.shape == (17, 32) and sin.shape == (17, 32)
+    one, zero = gen.f64_to_bf16_bits(1.0), gen.f64_to_bf16_bits(0.0)
+    for a in (0, 5, 14):
+        assert np.all(cos[a] == one) and np.all(sin[a] == zero)
+    c9, s9 = gen.rope_tables(9, 32)
+    assert np.array_equal(cos[5:14], c9) and np.array_equal(sin[5:14], s9)

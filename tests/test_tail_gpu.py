@@ -1,0 +1,108 @@
+"""GPU parity of the forward that cuts the last, partial round's query tiles into key ranges
+(``lsv_attn_fwd_tail``) against the fp64 oracle, through the C ABI.
+
+Same tolerances as the forward (bf16 O max-abs 2e-2, mean-abs 2e-3; LSE max-abs 1e-3). The
+tiles of the whole rounds are computed exactly as ``lsv_attn_fwd`` computes them, so their rows
+must be bit-identical to it; every row of the cut tiles is checked against the oracle. Small
+packs take small ``compute_units`` values so that their plans cut 2-8 ranges (including tail
+tiles that are empty or ragged, segments shorter than a range, and a pack with no whole tile);
+the 19,394 x 14 workload (cut) and the 4,096 x 56 one (left whole: its last round is half full)
+run with the device's own count, the plans the benchmark times.
+"""
+
+import numpy as np
+import pytest
+
+from long_sequence_video_amd import inputs as gen
+from tests.gpu_common import compare, from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_tail(inp, device, units=None, *, out_fill=None):
+    import torch
+    import long_sequence_video_amd as lsv
+    q, k, v = (to_dev(x, device) for x in (inp.q, inp.k, inp.v))
+    cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device)
+    out = torch.empty_like(q)
+    lse = torch.empty((inp.n_heads, inp.total_tokens), dtype=torch.float32, device=device)
+    if out_fill is not None:
+        out.view(torch.int16).fill_(int(np.int16(np.uint16(out_fill))))
+        lse.fill_(-7.0)
+    lsv.attn_fwd_tail(q, k, v, cu, inp.max_seqlen, inp.scale, compute_units=units, out=out, lse=lse)
+    ref_o, ref_l = lsv.attn_fwd(q, k, v, cu, inp.max_seqlen, inp.scale)
+    torch.cuda.synchronize(device)
+    return from_dev(out), lse.cpu().numpy(), from_dev(ref_o), ref_l.cpu().numpy()
+
+
+def tail_tiles(inp, units):
+    """The plan's (split, tail logical tiles): XCD x owns logical tiles [x P, (x + 1) P),
+    P = n / 8, and its last n_tail / 8 are the cut ones."""
+    import long_sequence_video_amd as lsv
+    split, n_tail = lsv.lsv_attn_fwd_tail_plan(len(inp.cu_seqlens) - 1, inp.max_seqlen, inp.n_heads, units)
+    n = (inp.max_seqlen + 255) // 256 * (len(inp.cu_seqlens) - 1) * inp.n_heads
+    per_xcd, t = n // 8, n_tail // 8
+    return split, [x * per_xcd + per_xcd - t + r for x in range(8) for r in range(t)]
+
+
+def whole_tile_rows(inp, units):
+    """(token, head) pairs of the query tiles that the plan leaves whole, as a boolean [T, H]."""
+    split, tail = tail_tiles(inp, units)
+    tiles = (inp.max_seqlen + 255) // 256
+    n_seqs = len(inp.cu_seqlens) - 1
+    whole = np.ones((inp.total_tokens, inp.n_heads), bool)
+    for logical in tail:
+        qt, hs = logical % tiles, logical // tiles
+        seg, head = hs % n_seqs, hs // n_seqs
+        a, b = int(inp.cu_seqlens[seg]), int(inp.cu_seqlens[seg + 1])
+        whole[a + 256 * qt:min(b, a + 256 * qt + 256), head] = False
+    return whole, split, len(tail)
+
+
+@pytest.mark.parametrize("seqlens,heads,units", [
+    ([5000], 8, 128),            # 20 tiles per XCD: the last 4 of each (one head's, ragged last), 4 ranges
+    ([8200], 8, 64),             # 33 per XCD: each head's last tile (8 rows), 8 ranges
+    ([9000, 300, 4097], 2, 96),  # 27 per XCD: 24 tail tiles, 12 of them empty, 4 ranges
+    ([9000, 300], 4, 256),       # 36 per XCD: 32 tail tiles (16 empty, 4 ragged), 8 ranges
+    ([1, 5000], 1, 256),         # 5 per XCD, all cut: no whole tile; the 1-token segment's ranges 2-4 are empty
+    ([2048, 300], 1, 256),       # 2 per XCD, all cut: 2 ranges, the 300-token segment's tiles among them
+    ([4000, 4000], 1, 128),      # 4 per XCD: 3 ranges
+])
+def test_tail_all_rows(gpu, seqlens, heads, units):
+    inp = gen.generate(seqlens, heads, seed=800 + len(seqlens) + units, name="tail")
+    whole, split, n_tail = whole_tile_rows(inp, units)
+    assert split > 1 and n_tail > 0
+    say(f"case tail {seqlens} h{heads} units {units}: {n_tail} tail tiles x {split} ranges")
+    out, lse, ref_o, ref_l = run_tail(inp, gpu, units)
+    assert np.array_equal(out[whole], ref_o[whole])
+    assert np.array_equal(lse.T[whole].view(np.uint32), ref_l.T[whole].view(np.uint32))
+    compare(inp, out, lse, label=f"tail {seqlens} h{heads} units {units}")
+
+
+def test_tail_rows_outside_segments_untouched(gpu):
+    """96 logical tiles on 88 units, 12 per XCD: the last of each is cut into 3 key ranges (4 of
+    them empty tiles of the short segments, 2 the ragged last tile of a 4,000-token segment);
+    NaN outside every segment."""
+    inp = gen.generate([61, 0, 4000], 2, seed=71, total_tokens=4100, name="tail_poison")
+    for t in (inp.q, inp.k, inp.v):
+        t[4061:] = 0x7FC0  # NaN outside every segment
+    say("case tail poison")
+    out, lse, _, _ = run_tail(inp, gpu, 88, out_fill=0x1234)
+    assert np.all(out[4061:] == 0x1234) and np.all(lse[:, 4061:] == -7.0)
+    compare(inp, out, lse, rows=np.arange(4061), label="tail poison")
+
+
+@pytest.mark.parametrize("name", ["sp4_share_s19394_h14", "s4096_h56_kboost"])
+def test_tail_workloads_every_row(gpu, name):
+    """The benchmark's plans (the device's compute units): every row against the oracle, whole
+    tiles bit-identical to lsv_attn_fwd, and two runs bit-identical."""
+    import long_sequence_video_amd as lsv
+    inp = gen.make_config(name)
+    units = lsv.lsv_device_peak(0)[1]
+    whole, split, n_tail = whole_tile_rows(inp, units)
+    say(f"case tail {name}: {n_tail} tail tiles x {split} ranges on {units} compute units")
+    out, lse, ref_o, ref_l = run_tail(inp, gpu)
+    assert np.array_equal(out[whole], ref_o[whole])
+    out2, lse2, _, _ = run_tail(inp, gpu)
+    assert np.array_equal(out, out2) and np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
+    compare(inp, out, lse, label=f"tail {name}")
