@@ -568,6 +568,29 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
     if (k_len <= 0) return;  // an empty range: the combine pass leaves it out
   }
 
+  // Epilogue destinations of the split and tail variants, fixed here so that two addresses and
+  // a stride stay live through the key loop rather than four buffers and the indices into them
+  // (which spilled). Row q0 + rr of the tile: O at o_dst + rr * o_stride, LSE at l_dst[rr].
+  [[maybe_unused]] char* o_dst = nullptr;
+  [[maybe_unused]] float* l_dst = nullptr;
+  [[maybe_unused]] int o_stride = 0;
+  if constexpr (kSplit || kTail) {
+    const int64_t tok0 = (int64_t)seg_start + q0;
+    if (kSplit) {  // [split][token][head][d] and [split][head][token]
+      o_dst = (char*)(part_o + (((int64_t)split * total_tokens + tok0) * n_heads + head) * kD);
+      o_stride = n_heads * kD * (int)sizeof(float);
+      l_dst = part_lse + ((int64_t)split * n_heads + head) * total_tokens + tok0;
+    } else if (piece >= 0) {  // [piece][row in tile][d] and [piece][row in tile]
+      o_dst = (char*)(part_o + (int64_t)piece * kBQ * kD);
+      o_stride = kD * (int)sizeof(float);
+      l_dst = part_lse + (int64_t)piece * kBQ;
+    } else {  // the output itself
+      o_dst = (char*)(o + (tok0 * n_heads + head) * kD);
+      o_stride = n_heads * kRowBytes;
+      l_dst = lse + (int64_t)head * total_tokens + tok0;
+    }
+  }
+
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const unsigned lds_base = (unsigned)(uintptr_t)(lds_char*)smem_generic;
@@ -638,10 +661,9 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
   if (row < seg_len) {
     const int64_t tok = (int64_t)seg_start + row;
     const float lse_row = (acc.m * c + __log2f(l)) * 0.69314718055994530942f;
+    const int rr = row - q0;
     if (kSplit || (kTail && piece >= 0)) {
-      const int64_t prow_idx = kTail ? (int64_t)piece * kBQ + (row - q0)
-                                     : ((int64_t)split * total_tokens + tok) * n_heads + head;
-      float* prow = part_o + prow_idx * kD;
+      float* prow = (float*)(o_dst + (int64_t)rr * o_stride);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -651,10 +673,9 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
           for (int e = 0; e < 4; ++e) w[e] = acc.O[db][4 * g + e] / lb;
           *(f32x4*)(prow + 32 * db + 8 * g + 4 * ln.h32) = w;
         }
-      if (ln.h32 == 0)
-        part_lse[kTail ? prow_idx : ((int64_t)split * n_heads + head) * total_tokens + tok] = lse_row;
+      if (ln.h32 == 0) l_dst[rr] = lse_row;
     } else {
-      uint16_t* orow = o + (tok * n_heads + head) * kD;
+      uint16_t* orow = kTail ? (uint16_t*)(o_dst + (int64_t)rr * o_stride) : o + (tok * n_heads + head) * kD;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -669,7 +690,12 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
           pk[1] = __builtin_bit_cast(unsigned, hi);
           *(u32x2*)(orow + 32 * db + 8 * g + 4 * ln.h32) = pk;
         }
-      if (ln.h32 == 0) lse[(int64_t)head * total_tokens + tok] = lse_row;
+      if (ln.h32 == 0) {
+        if (kTail)
+          l_dst[rr] = lse_row;
+        else
+          lse[(int64_t)head * total_tokens + tok] = lse_row;
+      }
     }
   }
 }
