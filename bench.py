@@ -81,9 +81,9 @@ def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def measured_traffic(workload: str, kernel_source: str = KERNEL_SOURCE, kernel: str = "attn_fwd"):
-    """(bytes per launch, summary path) from the committed counter summary, if it was taken
-    on the current kernel source; else (None, reason)."""
+def profile_fields(workload: str, kernel_source: str = KERNEL_SOURCE, kernel: str = "attn_fwd"):
+    """(machine-readable fields, summary path) of the committed counter summary for this
+    workload, if it was taken on the current kernel source; else (None, reason)."""
     path = TRAFFIC_SUMMARY.format(kernel=kernel, workload=workload)
     if not os.path.exists(path):
         return None, "no counter summary for this workload"
@@ -94,10 +94,29 @@ def measured_traffic(workload: str, kernel_source: str = KERNEL_SOURCE, kernel: 
             fields[key.strip()] = val.strip().strip("`")
     if fields.get("kernel_source_sha256") != kernel_source_sha256(kernel_source):
         return None, "counter summary predates the current kernel source"
+    return fields, os.path.relpath(path, ROOT)
+
+
+def measured_traffic(workload: str, kernel_source: str = KERNEL_SOURCE, kernel: str = "attn_fwd"):
+    """(HBM bytes per launch, summary path) from the committed counter summary, if it was taken
+    on the current kernel source; else (None, reason)."""
+    fields, src = profile_fields(workload, kernel_source, kernel)
+    if fields is None:
+        return None, src
     try:
-        return float(fields["hbm_bytes_per_launch"]), os.path.relpath(path, ROOT)
+        return float(fields["hbm_bytes_per_launch"]), src
     except (KeyError, ValueError):
         return None, "counter summary lacks hbm_bytes_per_launch"
+
+
+def measured_mfma_flops(workload: str, kernel_source: str, kernel: str):
+    """Matrix flops one launch executes (the SQ_INSTS_VALU_MFMA_MOPS_* counter x 512) from the
+    committed counter summary, if taken on the current kernel source; else None."""
+    fields, _ = profile_fields(workload, kernel_source, kernel)
+    try:
+        return float(fields["mfma_flops_executed_per_launch"]) if fields else None
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -259,8 +278,9 @@ def bench_fp8(name: str, steps: int, warmup: int):
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": "attn_fwd_fp8_kernel",
-                     # plus the weight-sum MFMA: half of a 32x32x64 per eight
-                     "mfma_flops_executed": f8.flops() * (17.0 / 16.0)},
+                     # SQ_INSTS_VALU_MFMA_MOPS_F8 x 512: the counted flops, the padding of the
+                     # last key tiles and the weight-sum MFMA
+                     "mfma_flops_executed": measured_mfma_flops(name, FP8_SOURCE, "attn_fwd_fp8")},
     }
 
 
@@ -559,12 +579,15 @@ def main():
     log(f"{args.config}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s, {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
 
     peak_at_clock, cus, khz = lsv.lsv_device_peak(0)
+    executed = None
     if isinstance(n_split, dict):
         kernel = "attn_fwd_tail_kernel"
         traffic, traffic_src = measured_traffic(inp.name, kernel="attn_fwd_tail")
+        executed = measured_mfma_flops(inp.name, KERNEL_SOURCE, "attn_fwd_tail")
     elif n_split == 1:
         kernel = "attn_fwd_kernel"
         traffic, traffic_src = measured_traffic(inp.name)
+        executed = measured_mfma_flops(inp.name, KERNEL_SOURCE, "attn_fwd")
     else:
         kernel = "attn_fwd_split_kernel + attn_fwd_combine_kernel"
         traffic, traffic_src = None, "not measured for the key-split launch"
@@ -609,6 +632,9 @@ def main():
             "traffic_source": traffic_src,
             "algorithmic_hbm_bytes": algorithmic_bytes,
             "kernel": kernel,
+            # SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 from the same counter summary: the counted flops
+            # plus the masked padding of partial tiles
+            "mfma_flops_executed": executed,
             "peak_at_reported_clock": round(peak_at_clock, 1),
             "compute_units": cus,
             "clock_mhz": khz // 1000,
