@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from long_sequence_video_amd import inputs as gen
-from tests.gpu_common import compare, from_dev, say, to_dev
+from tests.gpu_common import compare, from_dev, sample_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -106,3 +106,31 @@ def test_tail_workloads_every_row(gpu, name):
     out2, lse2, _, _ = run_tail(inp, gpu)
     assert np.array_equal(out, out2) and np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
     compare(inp, out, lse, label=f"tail {name}")
+
+
+@pytest.mark.parametrize("name", ["varlen_19394_38000_104000_h56", "h56_s104000"])
+def test_tail_full_size_as_the_benchmark_launches_it(gpu, name):
+    """The 161,394-token pack and its 104,000-token segment alone, in the launch the benchmark
+    times (the device's compute units): whole tiles bit-identical to lsv_attn_fwd; every row of
+    the cut tiles (the last tiles of a head in each XCD's range) plus the first and last tiles of
+    every segment and random rows against the oracle, on every head."""
+    import torch
+    import long_sequence_video_amd as lsv
+    if name == "h56_s104000":
+        inp = gen.generate([104000], 56, seed=1005, name=name)
+    else:
+        inp = gen.make_config(name)
+    units = lsv.lsv_device_peak(0)[1]
+    whole, split, n_tail = whole_tile_rows(inp, units)
+    assert split > 1 and n_tail > 0
+    say(f"case tail {name}: {n_tail} tail tiles x {split} ranges on {units} compute units")
+    out, lse, ref_o, ref_l = run_tail(inp, gpu)
+    assert np.array_equal(out[whole], ref_o[whole])
+    assert np.array_equal(lse.T[whole].view(np.uint32), ref_l.T[whole].view(np.uint32))
+    del ref_o, ref_l
+    cut = np.flatnonzero(~whole.all(axis=1))
+    rows = np.union1d(cut, sample_rows(inp, 16, seed=12, tile=32))
+    say(f"case tail {name}: oracle on {len(rows)} rows ({len(cut)} in cut tiles)")
+    compare(inp, out, lse, rows=rows, label=f"tail {name}")
+    del inp, out, lse
+    torch.cuda.empty_cache()
