@@ -227,6 +227,8 @@ __device__ __forceinline__ void softmax_all(const f32x16& S, bf16x8 (&P)[2], flo
 // with each LDS operand read two MFMAs ahead, the eight exp2 pairs of S(t) after the odd
 // MFMAs, and the copy of tile t + kAhead after MFMA 4. After an odd tile, tile t+3 is waited
 // for and the workgroup synchronises. No branches.
+constexpr int kReadAhead = 3;  // LDS operands are read this many MFMAs ahead of their use
+
 template <int U>
 __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const f32x16& Scur, f32x16& Snext,
                                           const bf16x8 (&Pprev)[2], bf16x8 (&Pcur)[2], float nmc,
@@ -238,8 +240,8 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
     if (n < 8) opnd[n] = tr_operand(ln.vaddr, vslot, n);
     else opnd[n] = lds_row(ln.kaddr[n - 8] + kslot);
   };
-  read(0);
-  read(1);
+#pragma unroll
+  for (int n = 0; n < kReadAhead; ++n) read(n);
   sched_fence();
   u32x4 p[2];
   f32x16 S = {};
@@ -247,7 +249,7 @@ __device__ __forceinline__ void fast_step(const Ctx& cx, int t, Acc& acc, const 
   for (int n = 0; n < 16; ++n) {
     if (n < 8) acc.O[n & 3] = mfma(opnd[n], Pprev[n >> 2], acc.O[n & 3]);
     else S = mfma(opnd[n], qr[n - 8], S);
-    if (n + 2 < 16) read(n + 2);
+    if (n + kReadAhead < 16) read(n + kReadAhead);
     if (n == 4) load_tile(cx, t + kAhead);
     if (n == 7) {
       acc.LBm = mfma_rowsum(sel, Pprev[0], acc.LBm);
