@@ -278,8 +278,8 @@ __device__ __forceinline__ void lb_tile(Acc& acc, const bf16x8& sel, const bf16x
 // Runs the whole key loop with a fixed per-row reference (the max of the first tile).
 // Returns false when any of this lane's sums or O values is not finite (inf or NaN: a p
 // overflowed, or two overflowed products of opposite sign met in one O element).
-__device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, const bf16x8 (&qr)[8],
-                                         const Lane& ln, const bf16x8& sel) {
+// The first kAhead tile copies of the key loop.
+__device__ __forceinline__ void prefetch(const Ctx& cx, int n_kt) {
   if (n_kt >= 2) {
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) load_tile(cx, t);
@@ -287,6 +287,13 @@ __device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, cons
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) load_tile_to(cx, t, (unsigned)t * kSlotBytes);
   }
+}
+
+// With kPrefetched, the caller has issued prefetch() already.
+template <bool kPrefetched = false>
+__device__ __forceinline__ bool run_fast(const Ctx& cx, int n_kt, Acc& acc, const bf16x8 (&qr)[8],
+                                         const Lane& ln, const bf16x8& sel) {
+  if (!kPrefetched) prefetch(cx, n_kt);
   wait_vmcnt<kOpsPerTile * (kAhead - 2)>();
   barrier_lds();
 #pragma unroll
@@ -622,7 +629,9 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
   ln.vaddr = tr_read_base(lds_base + kRingBytes, ln.lane);
 
   // Q^T operand: lane holds q[row][16 s + 8 h32 .. +7] for s = 0..7 (normalised and rotated
-  // on the way in for lsv_attn_fwd_qnorm).
+  // on the way in for lsv_attn_fwd_qnorm, whose key tiles are requested first so that their
+  // latency overlaps the Q loads and the normalisation).
+  if (kQNorm) prefetch(cx, n_kt);
   bf16x8 qr[8];
   {
     int row = q0 + wave * kWaveQ + ln.l32;
@@ -644,7 +653,7 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
 #pragma unroll
     for (int i = 0; i < 8; ++i) sel[i] = one ? (__bf16)1.0f : (__bf16)0.0f;
   }
-  const bool ok = run_fast(cx, n_kt, acc, qr, ln, sel);
+  const bool ok = run_fast<kQNorm>(cx, n_kt, acc, qr, ln, sel);
   // Workgroup-wide verdict: any overflowing row sends the whole workgroup down the exact path.
   lds_int* flags = (lds_int*)(uintptr_t)(lds_base + 2 * kRingBytes);
   if (tid < kWaves) flags[tid] = 0;
