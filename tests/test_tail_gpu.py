@@ -134,3 +134,26 @@ def test_tail_full_size_as_the_benchmark_launches_it(gpu, name):
     compare(inp, out, lse, rows=rows, label=f"tail {name}")
     del inp, out, lse
     torch.cuda.empty_cache()
+
+
+def test_tail_at_the_largest_supported_segment(gpu):
+    """299,593 x 56, the largest segment the 32-bit in-segment offsets allow, with the device's
+    plan (the last 5 tiles of one head per XCD cut into 6 ranges, so the cut ranges start deep
+    into the segment): whole tiles bit-identical to lsv_attn_fwd, every cut-tile row and the
+    first and last tiles against the oracle."""
+    import torch
+    import long_sequence_video_amd as lsv
+    inp = gen.generate([299_593], 56, seed=1006, name="max_segment_s299593_h56")
+    units = lsv.lsv_device_peak(0)[1]
+    whole, split, n_tail = whole_tile_rows(inp, units)
+    say(f"case tail max segment: {n_tail} tail tiles x {split} ranges on {units} compute units")
+    out, lse, ref_o, ref_l = run_tail(inp, gpu)
+    assert np.array_equal(out[whole], ref_o[whole])
+    assert np.array_equal(lse.T[whole].view(np.uint32), ref_l.T[whole].view(np.uint32))
+    del ref_o, ref_l
+    if n_tail:
+        cut = np.flatnonzero(~whole.all(axis=1))
+        rows = np.union1d(cut, sample_rows(inp, 4, seed=13, tile=32))
+        compare(inp, out, lse, rows=rows, label="tail max segment")
+    del inp, out, lse
+    torch.cuda.empty_cache()
