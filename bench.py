@@ -43,7 +43,7 @@ calibrations, not part of ``value``.
 
 roofline.traffic (HBM bytes per launch) comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
 summary committed under profiles/ for this workload, scaled by the same counters on a copy of
-known size; it is null when that summary was taken on a different kernel source.
+known size; it is null when that summary was taken on a different kernel source or device header.
 """
 
 from __future__ import annotations
@@ -53,6 +53,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -81,6 +82,26 @@ def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
+def kernel_device_headers(path: str = KERNEL_SOURCE) -> list:
+    """The device-code headers a kernel source includes from its own folder (tile_ops.h: the
+    MFMA, LDS and copy helpers). lsv.h, in include/, declares the C ABI only."""
+    here = os.path.dirname(path)
+    found = []
+    for line in open(path):
+        m = re.match(r'\s*#include\s+"([^"]+)"', line)
+        if m and os.path.exists(os.path.join(here, m.group(1))):
+            found.append(os.path.join(here, m.group(1)))
+    return found
+
+
+def kernel_headers_sha256(path: str = KERNEL_SOURCE) -> str:
+    """SHA-256 over the device headers of ``path``, in include order."""
+    h = hashlib.sha256()
+    for header in kernel_device_headers(path):
+        h.update(open(header, "rb").read())
+    return h.hexdigest()
+
+
 def profile_fields(workload: str, kernel_source: str = KERNEL_SOURCE, kernel: str = "attn_fwd"):
     """(machine-readable fields, summary path) of the committed counter summary for this
     workload, if it was taken on the current kernel source; else (None, reason)."""
@@ -91,9 +112,13 @@ def profile_fields(workload: str, kernel_source: str = KERNEL_SOURCE, kernel: st
     for line in open(path):
         if line.startswith("- ") and ":" in line:
             key, val = line[2:].split(":", 1)
-            fields[key.strip()] = val.strip().strip("`")
+            quoted = re.search(r"`([^`]*)`", val)
+            fields[key.strip()] = quoted.group(1) if quoted else val.strip()
     if fields.get("kernel_source_sha256") != kernel_source_sha256(kernel_source):
         return None, "counter summary predates the current kernel source"
+    if kernel_device_headers(kernel_source) and \
+            fields.get("kernel_headers_sha256") != kernel_headers_sha256(kernel_source):
+        return None, "counter summary predates the current device headers"
     return fields, os.path.relpath(path, ROOT)
 
 

@@ -27,6 +27,43 @@ def test_cpu_baseline_leg_reports_the_oracle_on_host_cores():
     assert res["value"] > 0 and res["cores"] >= 1 and res["sample"]
 
 
+def test_committed_counter_summaries_match_the_kernel_sources():
+    """Each committed HBM counter summary names the kernel source and device headers it was
+    taken on; bench.py reports its traffic only while both hashes still match."""
+    sys.path.insert(0, ROOT)
+    import bench
+    pack = "varlen_19394_38000_104000_h56"
+    for kernel, src, workload in (("attn_fwd_tail", bench.KERNEL_SOURCE, pack), ("attn_fwd", bench.KERNEL_SOURCE, pack),
+                                  ("attn_fwd_fp8", bench.FP8_SOURCE, pack),
+                                  ("qkv_prologue", bench.PROLOGUE_SOURCE, bench.PROLOGUE_CONFIG)):
+        traffic, where = bench.measured_traffic(workload, kernel_source=src, kernel=kernel)
+        assert traffic is not None and traffic > 0, (kernel, where)
+
+
+def test_counter_summary_is_stale_once_a_device_header_changes(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    src = tmp_path / "k.hip"
+    header = tmp_path / "tile_ops.h"
+    header.write_text("// helpers v1\n")
+    src.write_text('#include "lsv.h"\n#include "tile_ops.h"\n__global__ void k() {}\n')
+    assert bench.kernel_device_headers(str(src)) == [str(header)]
+    summary = tmp_path / "{kernel}_{workload}_hbm_traffic.md"
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(summary))
+    (tmp_path / "k_w_hbm_traffic.md").write_text(
+        f"- kernel_source_sha256: `{bench.kernel_source_sha256(str(src))}`\n"
+        f"- kernel_headers_sha256: `{bench.kernel_headers_sha256(str(src))}` (tile_ops.h)\n"
+        "- hbm_bytes_per_launch: `1.5e+09`\n")
+    assert bench.measured_traffic("w", kernel_source=str(src), kernel="k")[0] == 1.5e9
+    header.write_text("// helpers v2\n")
+    traffic, why = bench.measured_traffic("w", kernel_source=str(src), kernel="k")
+    assert traffic is None and "header" in why
+    header.write_text("// helpers v1\n")
+    src.write_text(src.read_text() + "// edited\n")
+    traffic, why = bench.measured_traffic("w", kernel_source=str(src), kernel="k")
+    assert traffic is None and "kernel source" in why
+
+
 @pytest.mark.gpu
 def test_bench_json_line(gpu):
     cmd = [sys.executable, BENCH, "--config", "tiny_s256_h4", "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
