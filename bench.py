@@ -610,9 +610,7 @@ def main():
         traffic, traffic_src = measured_traffic(inp.name, kernel="attn_fwd_tail")
         executed = measured_mfma_flops(inp.name, KERNEL_SOURCE, "attn_fwd_tail")
     elif n_split == 1:
-        # lsv_attn_fwd runs the tail kernel with nothing cut when the query tiles are a multiple of 8
-        n_tiles = (inp.max_seqlen + 255) // 256 * (len(inp.cu_seqlens) - 1) * inp.n_heads
-        kernel = "attn_fwd_tail_kernel (nothing cut)" if n_tiles % 8 == 0 else "attn_fwd_kernel"
+        kernel = "attn_fwd_tail_kernel (nothing cut)"   # what lsv_attn_fwd launches
         traffic, traffic_src = measured_traffic(inp.name)
         executed = measured_mfma_flops(inp.name, KERNEL_SOURCE, "attn_fwd")
     else:

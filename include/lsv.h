@@ -124,11 +124,12 @@ int lsv_attn_fwd_split(const void* q, const void* k, const void* v, void* o, flo
 
 /* The key split that lsv_attn_fwd_tail applies for these sizes on compute_units workgroup slots
  * (one workgroup of 256 query rows per compute unit, compute_units / 8 on each of the 8 XCDs).
- * With n = ceil(max_seqlen / 256) * n_seqs * n_heads query tiles, each XCD owns n / 8 consecutive
- * tiles, as in lsv_attn_fwd; the t = (n / 8) mod (compute_units / 8) of them past its last whole
- * round are cut into *n_split key ranges when t is at most a quarter of a round -- as many ranges
- * as fill the XCD's slots, at most 8, each of at least 1024 keys of a max_seqlen-key segment --
- * and *n_tail_tiles = 8 t. Otherwise, and whenever n is not a multiple of 8, *n_split = 1 and
+ * With n = ceil(max_seqlen / 256) * n_seqs * n_heads query tiles, each XCD owns P = ceil(n / 8)
+ * consecutive tiles, as in lsv_attn_fwd (the last XCD fewer when n is not a multiple of 8); the
+ * t = P mod (compute_units / 8) of them past its last whole round are cut into *n_split key
+ * ranges when t is at most a quarter of a round -- as many ranges as fill the XCD's slots, at
+ * most 8, each of at least 1024 keys of a max_seqlen-key segment -- and *n_tail_tiles = 8 t
+ * (counting the last XCD's missing tiles, which cost nothing). Otherwise *n_split = 1 and
  * *n_tail_tiles = 0 (nothing is cut). compute_units must be a positive multiple of 8 (256 on
  * MI355X; lsv_device_peak reports it). Host-only arithmetic; LSV_ERR_INVALID_ARG on bad sizes. */
 int lsv_attn_fwd_tail_plan(int32_t n_seqs, int32_t max_seqlen, int32_t n_heads, int32_t compute_units,

@@ -515,12 +515,13 @@ __device__ __forceinline__ void load_q_normed(const char* qrow, int64_t tok, int
 // with kSplit, against key range `split` of n_split; then O (bf16) and LSE are written, or,
 // with kSplit, this range's normalised fp32 O and its LSE into the partial buffers.
 //
-// With kTail (lsv_attn_fwd_tail; n_logical and n_tail multiples of 8): XCD x owns logical
-// tiles [x P, (x + 1) P), P = n_logical / 8, exactly as in the plain launch. Its first
-// P - n_tail / 8 tiles run whole, in the same order as there; its last n_tail / 8 tiles (its
-// last, partial round) are cut into n_split key ranges and run after them, on the same XCD.
-// Tail tile i = x * (n_tail / 8) + r and range s form piece s * n_tail + i, which writes its
-// range's fp32 O and LSE to row (piece * 256 + row in tile) of the partial buffers.
+// With kTail (lsv_attn_fwd_tail, and lsv_attn_fwd with n_tail = 0; n_tail a multiple of 8):
+// XCD x owns logical tiles [x P, (x + 1) P), P = ceil(n_logical / 8), exactly as in the plain
+// mapping (tiles from n_logical on do not exist). Its first P - n_tail / 8 tiles run whole, in
+// the same order as there; its last n_tail / 8 tiles (its last, partial round) are cut into
+// n_split key ranges and run after them, on the same XCD. Tail tile i = x * (n_tail / 8) + r
+// and range s form piece s * n_tail + i, which writes its range's fp32 O and LSE to row
+// (piece * 256 + row in tile) of the partial buffers.
 template <bool kSplit, bool kQNorm = false, bool kTail = false>
 __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
@@ -537,7 +538,9 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
   if (kTail) {
     const int xcd = blockIdx.x & 7;
     const int j = blockIdx.x >> 3;  // this block's place in its XCD's sequence
-    const int per_xcd = n_logical >> 3;
+    // Each XCD owns ceil(n_logical / 8) consecutive tiles; when n_logical is not a multiple of
+    // 8 the last XCD's range runs past the end, and those tiles (whole or cut) do not exist.
+    const int per_xcd = (n_logical + 7) >> 3;
     const int t = n_tail >> 3;
     if (j < per_xcd - t) {
       logical = xcd * per_xcd + j;
@@ -549,6 +552,7 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
       logical = xcd * per_xcd + per_xcd - t + r;
       piece = split * n_tail + xcd * t + r;
     }
+    if (logical >= n_logical) return;
   } else {
     const int per_xcd = gridDim.x >> 3;
     logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -707,15 +711,6 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
-                int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
-                int n_logical) {
-  fwd_body<false>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c, n_logical,
-                  1, nullptr, nullptr);
-}
-
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_qnorm_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                       uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                       int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
@@ -743,9 +738,9 @@ attn_fwd_tail_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 }
 
 // Combines the key ranges of the tail tiles of attn_fwd_tail_kernel: block i takes tail tile
-// i = x * (n_tail / 8) + r, the logical tile x P + P - n_tail / 8 + r (P = n_logical / 8), and
-// merges its rows' ranges as attn_fwd_combine_kernel does (the same segment checks; empty
-// ranges left out; fp32, then bf16 nearest even).
+// i = x * (n_tail / 8) + r, the logical tile x P + P - n_tail / 8 + r (P = ceil(n_logical / 8);
+// none from n_logical on), and merges its rows' ranges as attn_fwd_combine_kernel does (the
+// same segment checks; empty ranges left out; fp32, then bf16 nearest even).
 __global__ void __launch_bounds__(256)
 attn_fwd_tail_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                              uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -753,9 +748,10 @@ attn_fwd_tail_combine_kernel(const float* __restrict__ part_o, const float* __re
                              int n_heads, int64_t total_tokens, int n_logical, int n_tail, int n_split) {
   const int t = blockIdx.x;
   if (t >= n_tail) return;
-  const int per_xcd = n_logical >> 3;
+  const int per_xcd = (n_logical + 7) >> 3;
   const int tail_per_xcd = n_tail >> 3;
   const int logical = (t / tail_per_xcd + 1) * per_xcd - tail_per_xcd + t % tail_per_xcd;
+  if (logical >= n_logical) return;  // past the end of the last XCD's range
   const int qt = logical % tiles_per_seq;
   const int hs = logical / tiles_per_seq;
   const int seg = hs % n_seqs;
@@ -871,20 +867,19 @@ constexpr int kMaxSplit = 8;
 constexpr int kMinTailKeys = 1024;  // a tail tile's key ranges keep at least this many keys
 
 // The tail split of lsv_attn_fwd_tail for n_logical query tiles on `units` workgroup slots
-// (units / 8 per XCD). Each XCD owns n_logical / 8 consecutive tiles, as in the plain launch;
-// the t of them past its last whole round are cut into key ranges when t is at most a quarter
-// of a round, into as many ranges as fill the XCD's slots (at most kMaxSplit, and each of at
-// least kMinTailKeys keys of a max_seqlen-key segment). n_tail = 8 t. Nothing is cut (n_split
-// = 1, n_tail = 0) when n_logical is not a multiple of 8. (Measured on MI355X: a round half
+// (units / 8 per XCD). Each XCD owns P = ceil(n_logical / 8) consecutive tiles, as in the plain
+// launch (the last XCD fewer when n_logical is not a multiple of 8); the t = P mod (units / 8)
+// of them past its last whole round are cut into key ranges when t is at most a quarter of a
+// round, into as many ranges as fill the XCD's slots (at most kMaxSplit, and each of at least
+// kMinTailKeys keys of a max_seqlen-key segment). n_tail = 8 t. (Measured on MI355X: a round half
 // full costs less than a full one -- the idle half lets the busy half clock higher -- and
 // cutting it into 2 ranges gained nothing at 4,096 x 56; a round one-sixth full, at 19,394 x
 // 14, cut into 6 ranges gained 9%.)
 void tail_plan(int64_t n_logical, int32_t max_seqlen, int32_t units, int32_t* n_split, int64_t* n_tail) {
   *n_split = 1;
   *n_tail = 0;
-  if (n_logical % 8 != 0) return;
   const int64_t slots = units / 8;
-  const int64_t t = (n_logical / 8) % slots;
+  const int64_t t = ((n_logical + 7) / 8) % slots;
   if (t == 0 || t > slots / 4) return;
   int64_t split = slots / t;
   if (split > kMaxSplit) split = kMaxSplit;
@@ -959,24 +954,18 @@ int lsv_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   const int64_t grid = (n_logical + 7) / 8 * 8;
   if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
   const float c = (float)((double)scale * 1.4426950408889634074);
-  // With a multiple of 8 query tiles, the tail kernel with nothing cut: the same tiles on the
-  // same XCDs in the same order and the same arithmetic (bit-identical results), but its compiled
-  // loop issues the LDS operand reads further ahead, and it measured 0.8-1.4% faster on every
-  // workload here (same-box A/B, alternating).
-  const bool xcd_form = n_logical % 8 == 0;
-  const void* fn = xcd_form ? (const void*)attn_fwd_tail_kernel : (const void*)attn_fwd_kernel;
+  // The tail kernel with nothing cut: the plain launch's tiles, XCDs, order and arithmetic, and
+  // the compiled loop that measured 0.8-1.4% faster than a kernel of the same body with the
+  // plain mapping (its LDS operand reads are scheduled further ahead; same-box A/B).
   // The dynamic-LDS limit is a per-function attribute; setting it again is harmless.
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess) return LSV_ERR_HIP;
+  if (hipFuncSetAttribute((const void*)attn_fwd_tail_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return LSV_ERR_HIP;
   (void)hipGetLastError();
-  if (xcd_form)
-    hipLaunchKernelGGL(attn_fwd_tail_kernel, dim3((unsigned)n_logical), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens,
-                       (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical, 0, 1,
-                       (float*)nullptr, (float*)nullptr);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens,
-                       (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical);
+  hipLaunchKernelGGL(attn_fwd_tail_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens,
+                     (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical, 0, 1,
+                     (float*)nullptr, (float*)nullptr);
   if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
   return LSV_OK;
 }
@@ -1048,7 +1037,7 @@ int lsv_attn_fwd_tail(const void* q, const void* k, const void* v, void* o, floa
   if ((uintptr_t)workspace & 15) return LSV_ERR_ALIGNMENT;
   const int64_t pieces = n_tail * n_split;
   if (workspace_bytes < pieces * kBQ * (kD + 1) * (int64_t)sizeof(float)) return LSV_ERR_INVALID_ARG;
-  const int64_t grid = n_logical - n_tail + pieces;  // a multiple of 8: the plan cuts only then
+  const int64_t grid = (n_logical + 7) / 8 * 8 - n_tail + pieces;  // 8 x (blocks per XCD)
   if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
   if (hipFuncSetAttribute((const void*)attn_fwd_tail_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kLdsBytes) != hipSuccess)

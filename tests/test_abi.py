@@ -349,15 +349,19 @@ def test_norm_rope_validation_before_any_hip_call(args, code):
 
 
 def test_tail_plans():
-    """lsv_attn_fwd_tail's plans (host arithmetic): per XCD, n / 8 tiles, the ones past its last
-    whole round of compute_units / 8 cut when they are at most a quarter of it."""
+    """lsv_attn_fwd_tail's plans (host arithmetic): per XCD, ceil(n / 8) tiles, the ones past its
+    last whole round of compute_units / 8 cut when they are at most a quarter of it."""
     assert lsv.lsv_attn_fwd_tail_plan(1, 19394, 14, 256) == (6, 40)      # 1,064 tiles: 133 per XCD, 5 past
     assert lsv.lsv_attn_fwd_tail_plan(3, 104000, 56, 256) == (8, 24)     # the 161,394-token pack: 3 past
     assert lsv.lsv_attn_fwd_tail_plan(1, 104000, 56, 256) == (8, 8)      # 2,849 per XCD: 1 past
     assert lsv.lsv_attn_fwd_tail_plan(1, 4096, 56, 256) == (1, 0)        # 112 per XCD: half a round left whole
     assert lsv.lsv_attn_fwd_tail_plan(1, 38000, 56, 256) == (1, 0)       # 1,043 per XCD: 19 past, over a quarter
-    assert lsv.lsv_attn_fwd_tail_plan(1, 256, 4, 256) == (1, 0)          # 4 tiles: not a multiple of 8
-    assert lsv.lsv_attn_fwd_tail_plan(1, 5000, 1, 16) == (1, 0)          # 20 tiles: not a multiple of 8
+    assert lsv.lsv_attn_fwd_tail_plan(1, 256, 4, 256) == (1, 0)          # 4 tiles: ranges would be under 1,024 keys
+    assert lsv.lsv_attn_fwd_tail_plan(1, 5000, 1, 16) == (1, 0)          # 20 tiles, 3 per XCD on 2 slots: half a round
+    # n not a multiple of 8 (the sp=4 shares of the 38,000- and 104,000-token clips at 14 heads)
+    assert lsv.lsv_attn_fwd_tail_plan(1, 38000, 14, 256) == (6, 40)      # 2,086 tiles: 261 per XCD, 5 past
+    assert lsv.lsv_attn_fwd_tail_plan(1, 104000, 14, 256) == (1, 0)      # 5,698 tiles: 713 per XCD, 9 past
+    assert lsv.lsv_attn_fwd_tail_plan(1, 5000, 7, 128) == (4, 16)        # 140 tiles: 18 per XCD, 2 past
     assert lsv.lsv_attn_fwd_tail_plan(1, 1024, 8, 256) == (1, 0)         # ranges would be under 1,024 keys
     assert lsv.lsv_attn_fwd_tail_plan(2, 5000, 1, 256) == (4, 40)        # every tile cut: 5 per XCD of 32 slots
     assert lsv.lsv_attn_fwd_tail_plan(2, 9000, 4, 256) == (8, 32)

@@ -37,12 +37,13 @@ def run_tail(inp, device, units=None, *, out_fill=None):
 
 def tail_tiles(inp, units):
     """The plan's (split, tail logical tiles): XCD x owns logical tiles [x P, (x + 1) P),
-    P = n / 8, and its last n_tail / 8 are the cut ones."""
+    P = ceil(n / 8) (none from n on), and its last n_tail / 8 are the cut ones."""
     import long_sequence_video_amd as lsv
     split, n_tail = lsv.lsv_attn_fwd_tail_plan(len(inp.cu_seqlens) - 1, inp.max_seqlen, inp.n_heads, units)
     n = (inp.max_seqlen + 255) // 256 * (len(inp.cu_seqlens) - 1) * inp.n_heads
-    per_xcd, t = n // 8, n_tail // 8
-    return split, [x * per_xcd + per_xcd - t + r for x in range(8) for r in range(t)]
+    per_xcd, t = -(-n // 8), n_tail // 8
+    return split, [x * per_xcd + per_xcd - t + r for x in range(8) for r in range(t)
+                   if x * per_xcd + per_xcd - t + r < n]
 
 
 def whole_tile_rows(inp, units):
@@ -67,6 +68,10 @@ def whole_tile_rows(inp, units):
     ([1, 5000], 1, 256),         # 5 per XCD, all cut: no whole tile; the 1-token segment's ranges 2-4 are empty
     ([2048, 300], 1, 256),       # 2 per XCD, all cut: 2 ranges, the 300-token segment's tiles among them
     ([4000, 4000], 1, 128),      # 4 per XCD: 3 ranges
+    # query tiles not a multiple of 8: the last XCD's range runs past the end
+    ([5000], 7, 128),            # 140 tiles, 18 per XCD, the last 2 cut in 4 ranges; XCD 7's last 4 do not exist
+    ([4104], 7, 96),             # 119 tiles, 15 per XCD, the last 3 cut in 4 ranges; XCD 7's last one does not exist
+    ([3590, 1200], 1, 128),      # 30 tiles, 4 per XCD, all cut in 3 ranges; XCD 7's last 2 do not exist
 ])
 def test_tail_all_rows(gpu, seqlens, heads, units):
     inp = gen.generate(seqlens, heads, seed=800 + len(seqlens) + units, name="tail")
@@ -130,6 +135,34 @@ def test_tail_full_size_as_the_benchmark_launches_it(gpu, name):
     del ref_o, ref_l
     cut = np.flatnonzero(~whole.all(axis=1))
     rows = np.union1d(cut, sample_rows(inp, 16, seed=12, tile=32))
+    say(f"case tail {name}: oracle on {len(rows)} rows ({len(cut)} in cut tiles)")
+    compare(inp, out, lse, rows=rows, label=f"tail {name}")
+    del inp, out, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,seqlen,seed", [("sp4_share_s38000_h14", 38000, 1008),
+                                               ("sp4_share_s104000_h14", 104000, 1009)])
+def test_tail_sp4_shares_with_a_ragged_xcd_range(gpu, name, seqlen, seed):
+    """One sp=4 rank's 14-head share of the 38,000- and 104,000-token clips (RMS-normalised Q/K):
+    2,086 and 5,698 query tiles, not multiples of 8, so the last XCD's range runs past the end.
+    On 256 compute units 38,000 x 14 cuts the last 5 tiles of each XCD into 6 ranges, and
+    104,000 x 14 (9 tiles past its last round) runs whole, as lsv_attn_fwd. Whole tiles
+    bit-identical to lsv_attn_fwd; every cut-tile row, the first and last tiles of every
+    segment and random rows against the oracle, on every head."""
+    import torch
+    import long_sequence_video_amd as lsv
+    inp = gen.generate([seqlen], 14, seed=seed, rms_qk=True, name=name)
+    units = lsv.lsv_device_peak(0)[1]
+    whole, split, n_tail = whole_tile_rows(inp, units)
+    assert ((seqlen + 255) // 256 * 14) % 8 != 0
+    say(f"case tail {name}: {n_tail} tail tiles x {split} ranges on {units} compute units")
+    out, lse, ref_o, ref_l = run_tail(inp, gpu)
+    assert np.array_equal(out[whole], ref_o[whole])
+    assert np.array_equal(lse.T[whole].view(np.uint32), ref_l.T[whole].view(np.uint32))
+    del ref_o, ref_l
+    cut = np.flatnonzero(~whole.all(axis=1))
+    rows = np.union1d(cut, sample_rows(inp, 16, seed=14, tile=32))
     say(f"case tail {name}: oracle on {len(rows)} rows ({len(cut)} in cut tiles)")
     compare(inp, out, lse, rows=rows, label=f"tail {name}")
     del inp, out, lse
