@@ -44,7 +44,7 @@ def hip_flags() -> list[str]:
 
 
 def build_hip(verbose: bool = False) -> str:
-    tmp = HIP_LIB + ".tmp"
+    tmp = "%s.%d.tmp" % (HIP_LIB, os.getpid())  # one name per process: concurrent builds
     cmd = [hipcc(), *hip_flags(), *HIP_SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

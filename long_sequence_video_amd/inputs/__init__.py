@@ -40,7 +40,7 @@ _lib = None
 def build_library(verbose: bool = False) -> str:
     """Compile ``gen.c`` with gcc into ``liblsvgen.so`` (always recompiles)."""
     import subprocess
-    tmp = LIB_PATH + ".tmp"
+    tmp = "%s.%d.tmp" % (LIB_PATH, os.getpid())  # one name per process: concurrent builds
     include = os.path.join(os.path.dirname(os.path.dirname(_HERE)), "include")
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11", "-Wall", "-Werror",
            "-I", include, SOURCE_PATH, "-o", tmp, "-lm"]

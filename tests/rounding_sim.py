@@ -110,7 +110,7 @@ def _fp8_lib():
     if _sim is not None:
         return _sim
     if not os.path.exists(_SIM_LIB) or os.path.getmtime(_SIM_LIB) < os.path.getmtime(_SIM_SRC):
-        tmp = _SIM_LIB + ".tmp"
+        tmp = "%s.%d.tmp" % (_SIM_LIB, os.getpid())  # one name per process: parallel test workers
         subprocess.run(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Werror",
                         "-ffp-contract=off", "-o", tmp, _SIM_SRC, "-lm"], check=True)
         os.replace(tmp, _SIM_LIB)
