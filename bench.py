@@ -11,9 +11,12 @@ per step). Prints ONE JSON line on stdout; progress goes to stderr.
   python bench.py --copy-bytes N   # a plain device copy of N bytes, to calibrate HBM counters
 
 An object ``attn_fwd_fp8`` times the FP8 (e4m3) forward on the same pack quantised per tensor,
-with the same flop count, against MI355X's dense FP8 peak (5.0 PFLOP/s).
+with the same flop count, against MI355X's dense FP8 peak (5.0 PFLOP/s); with the default
+``--split auto`` it runs lsv_attn_fwd_fp8_tail, the launch that cuts the last, partial round of
+query tiles into key ranges when the plan cuts any. Its ``legs`` time the same on the sp=4 share
+(19,394 x 14), whose last round is one-sixth full.
 
-An object ``attn_bwd`` times the backward (dQ, dK, dV; deterministic, three kernels) on the
+An object ``attn_bwd`` times the backward (dQ, dK, dV; deterministic, two kernels) on the
 same pack, counted the usual way as 2.5 x the forward's flops (the five products of the
 textbook backward); its roofline.frac is stated on that count. The kernels execute seven
 products (the dQ pass recomputes S and dP instead of accumulating dQ with atomics), reported
@@ -210,7 +213,9 @@ def bench_qnorm(steps: int, warmup: int):
     """The forward with the QKV prologue in front of it on the 161,394-token pack x 56 heads
     (R = 96, each segment's own RoPE positions), two ways: the stacked prologue (Q, K, V planes)
     then the forward, and lsv_norm_rope on K then the forward with Q's norm and rotation in its
-    Q-tile load. Returns the JSON object (per-part times, and the prologue bytes each way)."""
+    Q-tile load. Both forwards are the headline's launch (the tail split on the device's compute
+    units: lsv_attn_fwd_tail and lsv_attn_fwd_qnorm_tail). Returns the JSON object (per-part
+    times, and the prologue bytes each way)."""
     import torch
     import long_sequence_video_amd as lsv
     from long_sequence_video_amd import inputs as gen
@@ -227,12 +232,15 @@ def bench_qnorm(steps: int, warmup: int):
     out = torch.empty_like(q)
     lse = torch.empty((h, t), dtype=torch.float32, device=dev)
     ms = inp.max_seqlen
+    _, n_cus, _ = lsv.lsv_device_peak(0)
+    ws = torch.empty(lsv.lsv_attn_fwd_tail_workspace_size(n_cus), dtype=torch.uint8, device=dev)
     parts = {
         "two_pass": [lambda: lsv.qkv_prologue(q, k, v, qw, kw, cos, sin, eps=inp.eps, out=stacked),
-                     lambda: lsv.attn_fwd(stacked[0], stacked[1], stacked[2], cu, ms, inp.scale, out=out, lse=lse)],
+                     lambda: lsv.attn_fwd_tail(stacked[0], stacked[1], stacked[2], cu, ms, inp.scale,
+                                               compute_units=n_cus, out=out, lse=lse, workspace=ws)],
         "fused_q": [lambda: lsv.norm_rope(k, kw, cos, sin, eps=inp.eps, out=kn),
                     lambda: lsv.attn_fwd_qnorm(q, kn, v, qw, cos, sin, cu, ms, inp.scale, eps=inp.eps, out=out,
-                                               lse=lse)],
+                                               lse=lse, compute_units=n_cus, workspace=ws)],
     }
     stream = torch.cuda.current_stream(dev)
     res = {}
@@ -258,16 +266,20 @@ def bench_qnorm(steps: int, warmup: int):
     res.update({"workload": inp.name, "rotary_dim": 96, "steps": steps,
                 "prologue_hbm_bytes": {"two_pass": 6 * plane, "fused_q": 2 * plane},
                 "attention_tflops_fused_q": round(inp.flops() / (res["fused_q"]["attention_ms"] * 1e-3) / 1e12, 2)})
-    del q, k, v, qw, kw, cos, sin, stacked, kn, out, lse
+    del q, k, v, qw, kw, cos, sin, stacked, kn, out, lse, ws
     torch.cuda.empty_cache()
     return res
 
 
 PEAK_FP8_TFLOPS = 5000.0  # MI355X published dense FP8 MFMA peak (5.0 PFLOP/s)
+FP8_LEG = "sp4_share_s19394_h14"  # the FP8 forward's second workload in the default run
 
 
-def bench_fp8(name: str, steps: int, warmup: int):
-    """Time the FP8 forward on workload ``name`` quantised per tensor; returns the JSON object."""
+def bench_fp8(name: str, steps: int, warmup: int, split="auto"):
+    """Time the FP8 forward on workload ``name`` quantised per tensor; returns the JSON object.
+    With ``split`` "auto" the launch is lsv_attn_fwd_fp8_tail (the last, partial round of query
+    tiles cut into key ranges when the plan cuts any, else lsv_attn_fwd_fp8); otherwise
+    lsv_attn_fwd_fp8."""
     import torch
     import long_sequence_video_amd as lsv
     from long_sequence_video_amd import inputs as gen
@@ -277,10 +289,18 @@ def bench_fp8(name: str, steps: int, warmup: int):
     cu = torch.from_numpy(f8.cu_seqlens).to(dev)
     out = torch.empty(f8.q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty((f8.n_heads, f8.total_tokens), dtype=torch.float32, device=dev)
+    _, n_cus, _ = lsv.lsv_device_peak(0)
+    ranges, tail_tiles = lsv.lsv_attn_fwd_tail_plan(len(f8.cu_seqlens) - 1, f8.max_seqlen, f8.n_heads, n_cus)
+    tail = split == "auto" and ranges > 1
+    ws = torch.empty(lsv.lsv_attn_fwd_tail_workspace_size(n_cus), dtype=torch.uint8, device=dev) if tail else None
 
     def step():
-        lsv.attn_fwd_fp8(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale, out=out,
-                         lse=lse)
+        if tail:
+            lsv.attn_fwd_fp8_tail(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale,
+                                  compute_units=n_cus, out=out, lse=lse, workspace=ws)
+        else:
+            lsv.attn_fwd_fp8(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale,
+                             out=out, lse=lse)
 
     for _ in range(warmup):
         step()
@@ -294,18 +314,21 @@ def bench_fp8(name: str, steps: int, warmup: int):
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
     tf = f8.flops() / (ms * 1e-3) / 1e12
-    log(f"{name} fp8: {ms:.3f} ms, {tf:.1f} TFLOP/s, {100 * tf / PEAK_FP8_TFLOPS:.1f}% of the FP8 peak")
-    traffic, traffic_src = measured_traffic(name, kernel_source=FP8_SOURCE, kernel="attn_fwd_fp8")
-    del q, k, v, out, lse
+    log(f"{name} fp8{' (tail split)' if tail else ''}: {ms:.3f} ms, {tf:.1f} TFLOP/s, "
+        f"{100 * tf / PEAK_FP8_TFLOPS:.1f}% of the FP8 peak")
+    kernel = "attn_fwd_fp8_tail" if tail else "attn_fwd_fp8"
+    traffic, traffic_src = measured_traffic(name, kernel_source=FP8_SOURCE, kernel=kernel)
+    del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
     return {
         "workload": name + " (e4m3, per-tensor descales)", "ms_per_step": round(ms, 4), "steps": steps,
+        "key_split": {"tail_ranges": ranges, "tail_tiles": tail_tiles} if tail else 1,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "traffic_source": traffic_src,
-                     "kernel": "attn_fwd_fp8_kernel",
+                     "kernel": kernel + "_kernel",
                      # SQ_INSTS_VALU_MFMA_MOPS_F8 x 512: the counted flops, the padding of the
                      # last key tiles and the weight-sum MFMA
-                     "mfma_flops_executed": measured_mfma_flops(name, FP8_SOURCE, "attn_fwd_fp8")},
+                     "mfma_flops_executed": measured_mfma_flops(name, FP8_SOURCE, kernel)},
     }
 
 
@@ -356,7 +379,7 @@ def bench_backward(name: str, steps: int, warmup: int):
         "frac_executed": round(tf_exec / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": "counted (2.5 x sum 4*S^2*H*D)",
-                     "kernels": ["bwd_prep_kernel", "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"]},
+                     "kernels": ["bwd_prep_kernel", "attn_bwd_kernel (dK/dV and dQ passes)"]},
     }
 
 
@@ -584,7 +607,8 @@ def main():
         print(json.dumps({"qkv_prologue": bench_prologue(args.steps, args.warmup)}), flush=True)
         return
     if args.fp8_only:
-        print(json.dumps({"attn_fwd_fp8": bench_fp8(args.config, args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"attn_fwd_fp8": bench_fp8(args.config, args.steps, args.warmup, args.split)}),
+              flush=True)
         return
     if args.bwd_only:
         print(json.dumps({"attn_bwd": bench_backward(args.config, args.steps, args.warmup)}), flush=True)
@@ -674,7 +698,11 @@ def main():
             by_name["fallback_s38000_h56"]["vs_fast_path"] = round(
                 by_name["fallback_s38000_h56"]["ms_per_step"] / by_name["h3_s38000_h56"]["ms_per_step"], 3)
     if not args.no_fp8:
-        result["attn_fwd_fp8"] = bench_fp8(args.config, min(max(args.steps, 3), 10), max(min(args.warmup, 2), 1))
+        result["attn_fwd_fp8"] = bench_fp8(args.config, min(max(args.steps, 3), 10), max(min(args.warmup, 2), 1),
+                                           args.split)
+        if not args.no_legs and args.config != FP8_LEG:
+            # one sp=4 rank's share: the launch whose last round the tail split fills
+            result["attn_fwd_fp8"]["legs"] = [bench_fp8(FP8_LEG, 100, 20, args.split)]
         if not args.no_gemm_ref:
             ref8 = bench_gemm_reference("fp8", steps=64)
             result["attn_fwd_fp8"]["mfma_reference"] = ref8

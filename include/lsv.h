@@ -96,6 +96,24 @@ int lsv_attn_fwd_qnorm(const void* q, const void* k, const void* v, const void* 
                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens,
                        int32_t n_heads, int32_t head_dim, float scale, void* stream);
 
+/* lsv_attn_fwd_qnorm launched as lsv_attn_fwd_tail launches the forward (asynchronous; one kernel,
+ * plus the combine pass when it cuts tiles): the same Q-side prologue in the Q-tile load, the
+ * query tiles of the whole rounds run as in lsv_attn_fwd_qnorm, and each XCD's tiles of its last,
+ * partial round are cut into the key ranges of lsv_attn_fwd_tail_plan and merged as there. The
+ * result is bit-identical to lsv_norm_rope(q) followed by lsv_attn_fwd_tail on the same
+ * compute_units. When nothing is cut this is lsv_attn_fwd_qnorm itself and the workspace is not
+ * used.
+ *
+ * q, k, v, q_weight, cos, sin, rotary_dim, eps, o, lse, cu_seqlens, n_seqs, max_seqlen,
+ * total_tokens, n_heads, head_dim, scale, stream: as for lsv_attn_fwd_qnorm.
+ * compute_units, workspace, workspace_bytes: as for lsv_attn_fwd_tail.
+ */
+int lsv_attn_fwd_qnorm_tail(const void* q, const void* k, const void* v, const void* q_weight, const void* cos,
+                            const void* sin, int32_t rotary_dim, float eps, void* o, float* lse,
+                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens,
+                            int32_t n_heads, int32_t head_dim, float scale, int32_t compute_units, void* workspace,
+                            int64_t workspace_bytes, void* stream);
+
 /* Workspace bytes lsv_attn_fwd_split needs for n_split key ranges: n_split partial rows of
  * head_dim + 1 fp32 values per (token, head), i.e. 4 * n_split * total_tokens * n_heads * 129;
  * 0 for n_split = 1. Returns -1 for a negative size, n_heads < 1 or n_split outside [1, 8]. */
@@ -185,12 +203,34 @@ int lsv_attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_
                      void* o, float* lse, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
                      int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale, void* stream);
 
+/* FP8 (e4m3) attention forward that fills the last, partial round of workgroups (asynchronous;
+ * one kernel, plus a small combine pass when it cuts tiles): the operation of lsv_attn_fwd_fp8,
+ * launched as lsv_attn_fwd_tail launches the BF16 forward. The query tiles of the whole rounds
+ * run as in lsv_attn_fwd_fp8 (bit-identical rows); each XCD's tiles of its last, partial round are
+ * cut into the key ranges of lsv_attn_fwd_tail_plan (the same plan: FP8 query tiles are also 256
+ * rows), each range's dequantised, normalised O kept in fp32 with its LSE, and merged per row:
+ *     LSE = ln sum_r exp(LSE_r),   O = sum_r exp(LSE_r - LSE) O_r   (fp32, then bf16 nearest even).
+ * Each range rounds its own weights to e4m3 against its own running max, so the cut rows differ
+ * from lsv_attn_fwd_fp8's by rounding only; deterministic. When nothing is cut this is
+ * lsv_attn_fwd_fp8 itself and the workspace is not used.
+ *
+ * q, k, v, descale_q, descale_k, descale_v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens,
+ * n_heads, head_dim, scale, stream: as for lsv_attn_fwd_fp8.
+ * compute_units, workspace, workspace_bytes: as for lsv_attn_fwd_tail
+ *              (lsv_attn_fwd_tail_workspace_size(compute_units) bytes always suffice).
+ */
+int lsv_attn_fwd_fp8_tail(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                          float descale_v, void* o, float* lse, const int32_t* cu_seqlens, int32_t n_seqs,
+                          int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale,
+                          int32_t compute_units, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Workspace bytes lsv_attn_bwd needs: two fp32 values per (head, token), i.e.
  * 8 * total_tokens * n_heads. Returns -1 for a negative size or n_heads < 1. */
 int64_t lsv_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads);
 
-/* Attention backward on the caller's stream (asynchronous; three kernels, no atomics: the
- * same inputs give bit-identical gradients on every run).
+/* Attention backward on the caller's stream (asynchronous; two kernels -- a statistics pass,
+ * then the dK/dV and dQ passes in one launch -- and no atomics: the same inputs give
+ * bit-identical gradients on every run).
  *
  * The operation (FastVideo #2049, diff of fastvideo/attention/utils/flash_attn_cute.py, the
  * varlen backward op: it takes q, k, v, out, dout, lse, the softmax scale, causal=False and

@@ -8,9 +8,9 @@ Thin ctypes binding over the C ABI in ``include/lsv.h`` (``liblsv.so``, built in
 ``lsv_attn_bwd``, ``lsv_attn_bwd_workspace_size``, ``lsv_attn_bwd_noalloc``,
 ``lsv_attn_bwd_noalloc_max_rows``, ``lsv_qkv_prologue``, ``lsv_attn_fwd_qnorm``, ``lsv_norm_rope``,
 ``lsv_attn_fwd_tail``, ``lsv_attn_fwd_tail_plan``, ``lsv_attn_fwd_tail_workspace_size``,
-``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only marshal arguments;
-``attn_fwd``, ``attn_fwd_split``, ``attn_fwd_tail``, ``attn_fwd_fp8``, ``attn_bwd``,
-``attn_bwd_noalloc``, ``qkv_prologue``, ``attn_fwd_qnorm`` and ``norm_rope`` add torch-tensor conveniences (shape checks, output and workspace allocation, the current
+``lsv_attn_fwd_fp8_tail``, ``lsv_attn_fwd_qnorm_tail``, ``lsv_status_string``, ``lsv_device_peak``, ``lsv_tile_config``) only marshal arguments;
+``attn_fwd``, ``attn_fwd_split``, ``attn_fwd_tail``, ``attn_fwd_fp8``, ``attn_fwd_fp8_tail``, ``attn_bwd``,
+``attn_bwd_noalloc``, ``qkv_prologue``, ``attn_fwd_qnorm`` (and its ``compute_units`` form) and ``norm_rope`` add torch-tensor conveniences (shape checks, output and workspace allocation, the current
 stream). There is no fallback: if the library is missing or a call fails, an exception is
 raised.
 
@@ -32,7 +32,7 @@ __all__ = [
     "lsv_attn_fwd_fp8", "attn_fwd_fp8", "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_attn_bwd_noalloc",
     "lsv_attn_bwd_noalloc_max_rows", "attn_bwd_noalloc", "lsv_qkv_prologue", "lsv_attn_fwd_qnorm", "lsv_norm_rope",
     "attn_fwd_qnorm", "norm_rope", "lsv_attn_fwd_tail", "lsv_attn_fwd_tail_plan", "lsv_attn_fwd_tail_workspace_size",
-    "attn_fwd_tail",
+    "attn_fwd_tail", "lsv_attn_fwd_fp8_tail", "attn_fwd_fp8_tail", "lsv_attn_fwd_qnorm_tail",
     "lsv_status_string", "lsv_device_peak", "lsv_tile_config", "attn_fwd", "attn_fwd_split", "choose_split",
     "attn_bwd", "qkv_prologue", "flops", "EXPORTED_SYMBOLS",
 ]
@@ -42,7 +42,8 @@ EXPORTED_SYMBOLS = ("lsv_attn_fwd", "lsv_attn_fwd_split", "lsv_attn_fwd_split_wo
                     "lsv_attn_bwd", "lsv_attn_bwd_workspace_size", "lsv_attn_bwd_noalloc",
                     "lsv_attn_bwd_noalloc_max_rows", "lsv_qkv_prologue", "lsv_attn_fwd_qnorm", "lsv_norm_rope",
                     "lsv_attn_fwd_tail", "lsv_attn_fwd_tail_plan", "lsv_attn_fwd_tail_workspace_size",
-                    "lsv_status_string", "lsv_device_peak", "lsv_tile_config")
+                    "lsv_attn_fwd_fp8_tail", "lsv_attn_fwd_qnorm_tail", "lsv_status_string", "lsv_device_peak",
+                    "lsv_tile_config")
 
 LSV_OK = 0
 LSV_ERR_INVALID_ARG = -1
@@ -80,6 +81,13 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m long_sequence_video_amd.build`")
+    # torch ships its own HIP runtime. Loaded first, it also serves this library (same soname);
+    # loaded after it, the library would have mapped the system's copy as well, and the two
+    # runtimes in one process do not share devices, streams or memory.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.lsv_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, vp]
@@ -92,6 +100,8 @@ def load_library(path: str = LIB_PATH):
     f = ctypes.c_float
     lib.lsv_attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i32, i32, i64, i32, i32, f, vp]
     lib.lsv_attn_fwd_fp8.restype = ctypes.c_int
+    lib.lsv_attn_fwd_fp8_tail.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i32, i32, i64, i32, i32, f, i32, vp, i64, vp]
+    lib.lsv_attn_fwd_fp8_tail.restype = ctypes.c_int
     lib.lsv_attn_bwd.argtypes = [vp] * 10 + [i32, i32, i64, i32, i32, ctypes.c_float, vp, i64, vp]
     lib.lsv_attn_bwd.restype = ctypes.c_int
     lib.lsv_attn_bwd_workspace_size.argtypes = [i64, i32]
@@ -105,6 +115,9 @@ def load_library(path: str = LIB_PATH):
     lib.lsv_attn_fwd_qnorm.argtypes = [vp] * 6 + [i32, ctypes.c_float, vp, vp, vp, i32, i32, i64, i32, i32,
                                        ctypes.c_float, vp]
     lib.lsv_attn_fwd_qnorm.restype = ctypes.c_int
+    lib.lsv_attn_fwd_qnorm_tail.argtypes = [vp] * 6 + [i32, ctypes.c_float, vp, vp, vp, i32, i32, i64, i32, i32,
+                                            ctypes.c_float, i32, vp, i64, vp]
+    lib.lsv_attn_fwd_qnorm_tail.restype = ctypes.c_int
     lib.lsv_norm_rope.argtypes = [vp] * 5 + [i64, i32, i32, i32, ctypes.c_float, vp]
     lib.lsv_norm_rope.restype = ctypes.c_int
     lib.lsv_attn_fwd_tail.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, ctypes.c_float, i32, vp, i64,
@@ -185,6 +198,16 @@ def lsv_attn_fwd_fp8(q: int, k: int, v: int, descale_q: float, descale_k: float,
                                            max_seqlen, total_tokens, n_heads, head_dim, scale, stream)
 
 
+def lsv_attn_fwd_fp8_tail(q: int, k: int, v: int, descale_q: float, descale_k: float, descale_v: float, o: int,
+                          lse: int, cu_seqlens: int, n_seqs: int, max_seqlen: int, total_tokens: int, n_heads: int,
+                          head_dim: int, scale: float, compute_units: int, workspace: int, workspace_bytes: int,
+                          stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_fwd_fp8_tail(q, k, v, descale_q, descale_k, descale_v, o, lse, cu_seqlens,
+                                                n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                                                compute_units, workspace, workspace_bytes, stream)
+
+
 def lsv_attn_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, cu_seqlens: int,
                  n_seqs: int, max_seqlen: int, total_tokens: int, n_heads: int, head_dim: int, scale: float,
                  workspace: int, workspace_bytes: int, stream: int | None) -> int:
@@ -224,6 +247,16 @@ def lsv_attn_fwd_qnorm(q: int, k: int, v: int, q_weight: int, cos: int, sin: int
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().lsv_attn_fwd_qnorm(q, k, v, q_weight, cos, sin, rotary_dim, eps, o, lse, cu_seqlens,
                                              n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale, stream)
+
+
+def lsv_attn_fwd_qnorm_tail(q: int, k: int, v: int, q_weight: int, cos: int, sin: int, rotary_dim: int,
+                            eps: float, o: int, lse: int, cu_seqlens: int, n_seqs: int, max_seqlen: int,
+                            total_tokens: int, n_heads: int, head_dim: int, scale: float, compute_units: int,
+                            workspace: int, workspace_bytes: int, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().lsv_attn_fwd_qnorm_tail(q, k, v, q_weight, cos, sin, rotary_dim, eps, o, lse, cu_seqlens,
+                                                  n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                                                  compute_units, workspace, workspace_bytes, stream)
 
 
 def lsv_norm_rope(x: int, weight: int, cos: int, sin: int, out: int, total_tokens: int, n_heads: int,
@@ -661,7 +694,8 @@ def norm_rope(x, weight, cos=None, sin=None, *, eps: float = 1e-5, out=None, str
 
 
 def attn_fwd_qnorm(q, k, v, q_weight, cos, sin, cu_seqlens, max_seqlen: int | None = None,
-                   scale: float | None = None, *, eps: float = 1e-5, out=None, lse=None, stream=None):
+                   scale: float | None = None, *, eps: float = 1e-5, out=None, lse=None, stream=None,
+                   compute_units: int | None = None, workspace=None):
     """Attention forward with Q's RMSNorm + partial RoPE applied in the kernel's Q-tile load.
 
     Args:
@@ -670,9 +704,13 @@ def attn_fwd_qnorm(q, k, v, q_weight, cos, sin, cu_seqlens, max_seqlen: int | No
       q_weight: bfloat16 ``[128]``; cos, sin: bfloat16 ``[total_tokens, R]`` per-token tables,
         or None (R = 0).
       cu_seqlens, max_seqlen, scale, out, lse, stream: as for ``attn_fwd``; eps the RMSNorm epsilon.
+      compute_units, workspace: when ``compute_units`` is given, the launch is
+        ``lsv_attn_fwd_qnorm_tail`` (the last, partial round of query tiles cut into key ranges),
+        with ``workspace`` as for ``attn_fwd_tail``.
 
     Returns:
-      ``(out, lse)``, equal bit for bit to ``attn_fwd(norm_rope(q, q_weight, cos, sin), k, v, ...)``.
+      ``(out, lse)``, equal bit for bit to ``attn_fwd(norm_rope(q, q_weight, cos, sin), k, v, ...)``
+      (to ``attn_fwd_tail(norm_rope(q, ...), ..., compute_units=...)`` with ``compute_units``).
     """
     import torch
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
@@ -706,31 +744,34 @@ def attn_fwd_qnorm(q, k, v, q_weight, cos, sin, cu_seqlens, max_seqlen: int | No
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's GPU")
     if lse.shape != (heads, total) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != dev:
         raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor on q's GPU")
+    if compute_units is not None:
+        need = lsv_attn_fwd_tail_workspace_size(compute_units)
+        if need < 0:
+            raise ValueError("compute_units must be a positive multiple of 8")
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            mine.append(workspace)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous buffer on the same GPU")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     _keep_for(s, *mine)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), q_weight.data_ptr(), 0 if cos is None else cos.data_ptr(),
+            0 if sin is None else sin.data_ptr(), rd, eps, out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(),
+            cu_seqlens.numel() - 1, max_seqlen, total, heads, dim, scale)
     with torch.cuda.device(dev):
-        rc = lsv_attn_fwd_qnorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_weight.data_ptr(),
-                                0 if cos is None else cos.data_ptr(), 0 if sin is None else sin.data_ptr(), rd, eps,
-                                out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
-                                max_seqlen, total, heads, dim, scale, s.cuda_stream)
+        if compute_units is None:
+            rc = lsv_attn_fwd_qnorm(*args, s.cuda_stream)
+        else:
+            rc = lsv_attn_fwd_qnorm_tail(*args, compute_units, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), s.cuda_stream)
     if rc != LSV_OK:
-        raise LsvError(rc, "lsv_attn_fwd_qnorm")
+        raise LsvError(rc, "lsv_attn_fwd_qnorm" if compute_units is None else "lsv_attn_fwd_qnorm_tail")
     return out, lse
 
 
-def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, cu_seqlens,
-                 max_seqlen: int | None = None, scale: float | None = None, *, out=None, lse=None, stream=None):
-    """FP8 attention forward on torch tensors (one GPU).
-
-    Args:
-      q8, k8, v8: ``[total_tokens, n_heads, 128]`` e4m3 bytes (``torch.uint8`` or
-        ``torch.float8_e4m3fn``), contiguous.
-      descale_q, descale_k, descale_v: per-tensor descales (real value = descale * byte value).
-      cu_seqlens, max_seqlen, scale, out, lse, stream: as for ``attn_fwd``.
-
-    Returns:
-      ``(out, lse)``: bfloat16 ``[T, H, 128]`` and float32 ``[H, T]``.
-    """
+def _fp8_args(q8, k8, v8, cu_seqlens, max_seqlen, scale, out, lse):
+    """Checks the FP8 forward's tensors and fills in the defaults; returns
+    (max_seqlen, scale, out, lse, the buffers allocated here)."""
     import torch
     tensors = (q8, k8, v8)
     if any(t.element_size() != 1 or t.is_floating_point() and t.dtype != torch.float8_e4m3fn for t in tensors):
@@ -763,6 +804,26 @@ def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: floa
         raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
     if out.device != dev or lse.device != dev:
         raise ValueError("out and lse must be on the same GPU as q8")
+    return max_seqlen, scale, out, lse, mine
+
+
+def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, cu_seqlens,
+                 max_seqlen: int | None = None, scale: float | None = None, *, out=None, lse=None, stream=None):
+    """FP8 attention forward on torch tensors (one GPU).
+
+    Args:
+      q8, k8, v8: ``[total_tokens, n_heads, 128]`` e4m3 bytes (``torch.uint8`` or
+        ``torch.float8_e4m3fn``), contiguous.
+      descale_q, descale_k, descale_v: per-tensor descales (real value = descale * byte value).
+      cu_seqlens, max_seqlen, scale, out, lse, stream: as for ``attn_fwd``.
+
+    Returns:
+      ``(out, lse)``: bfloat16 ``[T, H, 128]`` and float32 ``[H, T]``.
+    """
+    import torch
+    max_seqlen, scale, out, lse, mine = _fp8_args(q8, k8, v8, cu_seqlens, max_seqlen, scale, out, lse)
+    dev = q8.device
+    total, heads, dim = q8.shape
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     _keep_for(s, *mine)
     with torch.cuda.device(dev):
@@ -771,4 +832,36 @@ def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: floa
                               max_seqlen, total, heads, dim, scale, s.cuda_stream)
     if rc != LSV_OK:
         raise LsvError(rc, "lsv_attn_fwd_fp8")
+    return out, lse
+
+
+def attn_fwd_fp8_tail(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, cu_seqlens,
+                      max_seqlen: int | None = None, scale: float | None = None, *, compute_units: int | None = None,
+                      out=None, lse=None, workspace=None, stream=None):
+    """FP8 attention forward that cuts the query tiles of the last, partial round of workgroups
+    into key ranges (``lsv_attn_fwd_fp8_tail``). Arguments as for ``attn_fwd_fp8``;
+    ``compute_units`` and ``workspace`` as for ``attn_fwd_tail``. Returns ``(out, lse)``."""
+    import torch
+    max_seqlen, scale, out, lse, mine = _fp8_args(q8, k8, v8, cu_seqlens, max_seqlen, scale, out, lse)
+    dev = q8.device
+    total, heads, dim = q8.shape
+    if compute_units is None:
+        compute_units = lsv_device_peak(dev.index if dev.index is not None else torch.cuda.current_device())[1]
+    need = lsv_attn_fwd_tail_workspace_size(compute_units)
+    if need < 0:
+        raise ValueError("compute_units must be a positive multiple of 8")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        mine.append(workspace)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous buffer on the same GPU")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _keep_for(s, *mine)
+    with torch.cuda.device(dev):
+        rc = lsv_attn_fwd_fp8_tail(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), descale_q, descale_k, descale_v,
+                                   out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                   max_seqlen, total, heads, dim, scale, compute_units, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), s.cuda_stream)
+    if rc != LSV_OK:
+        raise LsvError(rc, "lsv_attn_fwd_fp8_tail")
     return out, lse

@@ -7,10 +7,11 @@
 //   D_i = dO_i . O_i,   dS_ij = P_ij (dO_i . v_j - D_i),
 //   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i,   dV_j = sum_i P_ij dO_i.
 //
-// Design (gfx950, wave64), three kernels on the caller's stream, no atomics (deterministic):
+// Design (gfx950, wave64), two kernels on the caller's stream (prep, then the dK/dV and dQ
+// passes in one launch), no atomics (deterministic):
 //  * prep: -LSE / scale and -D per (head, token) into the workspace (16 lanes per row, like
 //    the other row-streaming passes). In raw score units, P = exp2(log2(e) scale (s - LSE /
-//    scale)), so the dK/dV kernel starts its S accumulator at -LSE / scale and its dP
+//    scale)), so the dK/dV pass starts its S accumulator at -LSE / scale and its dP
 //    accumulator at -D: the products come out as s - LSE / scale and dP - D, and each
 //    element then costs one multiply and one exp2 for P and one multiply for dS.
 //  * dK/dV: one workgroup = 8 waves = 256 keys of one (segment, head); each wave owns 32 keys
@@ -23,6 +24,8 @@
 //  * dQ: one workgroup = 256 queries; K and V tiles of 32 keys stream through the ring (K in
 //    both layouts, V in the row layout); S^T = K Q^T and dP^T = V dO^T give a lane one query
 //    and 16 keys, dS^T in bf16 is the B operand of dQ^T += K^T dS^T.
+//  * The two passes are independent, so they share one launch, dQ blocks after dK/dV blocks:
+//    a launch with few tiles then has one partly idle last round instead of two.
 //  * Copies are 16-byte global -> LDS transfers issued three tiles ahead; the last, partial
 //    tile of a segment is read shifted back to end at the segment end and its re-read rows
 //    are masked (segments shorter than 32 rows repeat their last row instead).
@@ -91,17 +94,17 @@ __device__ __forceinline__ void pack_pair(u32x4 (&P)[2], int j, float a, float b
   P[j >> 2][j & 3] = __builtin_bit_cast(unsigned, pp);
 }
 
-// Workgroup -> (head, segment, 256-row tile), XCD-aware: hardware dispatches block b to XCD
-// b % 8; each XCD gets a contiguous range of logical tiles (head-major, then segment).
+// Block b of a pass -> (head, segment, 256-row tile), XCD-aware: hardware dispatches block b
+// to XCD b % 8 (a pass starts at a multiple of 8); each XCD gets a contiguous range of
+// per_xcd logical tiles (head-major, then segment).
 struct Work {
   int head, seg_start, seg_len, r0;
   bool ok;
 };
-__device__ __forceinline__ Work map_block(const int32_t* cu_seqlens, int n_seqs, int tiles_per_seq, int max_seqlen,
-                                          int64_t total_tokens, int n_logical) {
+__device__ __forceinline__ Work map_block(int b, int per_xcd, const int32_t* cu_seqlens, int n_seqs,
+                                          int tiles_per_seq, int max_seqlen, int64_t total_tokens, int n_logical) {
   Work w;
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int logical = (b & 7) * per_xcd + (b >> 3);
   w.ok = false;
   if (logical >= n_logical) return w;
   const int rt = logical % tiles_per_seq;
@@ -256,14 +259,13 @@ __device__ __forceinline__ void dq_step(const DqCtx& cx, const DqLane& ln, int t
   }
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                   const uint16_t* __restrict__ dout, const float* __restrict__ ws_nl, const float* __restrict__ ws_d,
-                   uint16_t* __restrict__ dq, const int32_t* __restrict__ cu_seqlens, int n_seqs, int tiles_per_seq,
-                   int max_seqlen, int n_heads, int64_t total_tokens, float c, float scale, int n_logical) {
+// dQ for the 256 queries of work item w.
+__device__ __forceinline__ void dq_body(const Work& w, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                                        const float* __restrict__ ws_nl, const float* __restrict__ ws_d,
+                                        uint16_t* __restrict__ dq, int n_heads, int64_t total_tokens, float c,
+                                        float scale) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
-  const Work w = map_block(cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, total_tokens, n_logical);
-  if (!w.ok) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const unsigned lds_base = (unsigned)(uintptr_t)(lds_char*)smem_generic;
@@ -498,15 +500,14 @@ __device__ __forceinline__ void store_rows_t(uint16_t* orow, const f32x16 (&acc)
     }
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                     const uint16_t* __restrict__ dout, const float* __restrict__ ws_nl,
-                     const float* __restrict__ ws_d, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                     const int32_t* __restrict__ cu_seqlens, int n_seqs, int tiles_per_seq, int max_seqlen,
-                     int n_heads, int64_t total_tokens, float c, float scale, int n_logical) {
+// dK and dV for the 256 keys of work item w.
+__device__ __forceinline__ void dkdv_body(const Work& w, const uint16_t* __restrict__ q,
+                                          const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                          const uint16_t* __restrict__ dout, const float* __restrict__ ws_nl,
+                                          const float* __restrict__ ws_d, uint16_t* __restrict__ dk,
+                                          uint16_t* __restrict__ dv, int n_heads, int64_t total_tokens, float c,
+                                          float scale) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
-  const Work w = map_block(cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, total_tokens, n_logical);
-  if (!w.ok) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -586,6 +587,31 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
+// Both gradient passes in one launch: blocks [0, 8 P) are the dK/dV pass and blocks [8 P, 16 P)
+// the dQ pass (P = ceil(n_logical / 8) blocks per XCD in each; the second pass starts at a
+// multiple of 8, so its blocks keep their XCDs, and XCD x's tiles of both passes are the same
+// (head, segment) tiles). The passes are independent (both read only the inputs and the prep
+// kernel's statistics), and the dQ blocks, dispatched after the dK/dV ones, fill the compute
+// units that the dK/dV pass's last, partial round leaves idle. LDS: the larger of the two
+// passes' (the dK/dV ring).
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                const uint16_t* __restrict__ dout, const float* __restrict__ ws_nl, const float* __restrict__ ws_d,
+                uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                const int32_t* __restrict__ cu_seqlens, int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads,
+                int64_t total_tokens, float c, float scale, int n_logical) {
+  const int per_xcd = (n_logical + 7) >> 3;
+  const int b = blockIdx.x;
+  if (b < 8 * per_xcd) {
+    const Work w = map_block(b, per_xcd, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, total_tokens, n_logical);
+    if (w.ok) dkdv_body(w, q, k, v, dout, ws_nl, ws_d, dk, dv, n_heads, total_tokens, c, scale);
+  } else {
+    const Work w =
+        map_block(b - 8 * per_xcd, per_xcd, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, total_tokens, n_logical);
+    if (w.ok) dq_body(w, q, k, v, dout, ws_nl, ws_d, dq, n_heads, total_tokens, c, scale);
+  }
+}
+
 // File-scope scratch for lsv_attn_bwd_noalloc: the prep kernel's two fp32 values per (head,
 // token) for callers that cannot allocate. 2^27 bytes hold 2^24 (token, head) rows, e.g. one
 // 299,593-token segment at 56 heads, the largest the 32-bit offsets allow. Each GPU the library
@@ -646,11 +672,11 @@ int bwd_checks(const void* q, const void* k, const void* v, const void* o, const
       (int64_t)max_seqlen * row_stride + kRowBytes > (int64_t)UINT32_MAX)
     return LSV_ERR_UNSUPPORTED;
   const int64_t tiles = ((int64_t)max_seqlen + kBlockRows - 1) / kBlockRows;
-  if ((tiles * n_seqs * (int64_t)n_heads + 7) / 8 * 8 > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  if (2 * ((tiles * n_seqs * (int64_t)n_heads + 7) / 8 * 8) > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
   return kProceed;
 }
 
-// The three kernels on `stream`, with the stats in ws (2 * total_tokens * n_heads floats, fully
+// The two kernels on `stream`, with the stats in ws (2 * total_tokens * n_heads floats, fully
 // overwritten by the prep kernel before the other two read them). Arguments already checked.
 int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
@@ -658,10 +684,9 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
   const int64_t tiles = ((int64_t)max_seqlen + kBlockRows - 1) / kBlockRows;
   const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
   const int64_t grid = (n_logical + 7) / 8 * 8;
-  if (hipFuncSetAttribute((const void*)attn_bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kDqLds) !=
-          hipSuccess ||
-      hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          kDkvLds) != hipSuccess)
+  static_assert(kDkvLds >= kDqLds, "the merged launch sizes LDS for the dK/dV pass");
+  if (hipFuncSetAttribute((const void*)attn_bwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kDkvLds) !=
+      hipSuccess)
     return LSV_ERR_HIP;
   float* ws_nl = ws;
   float* ws_d = ws_nl + total_tokens * (int64_t)n_heads;
@@ -673,14 +698,10 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)prep_grid), dim3(256), 0, st, (const u32x4*)o,
                      (const u32x4*)dout, lse, ws_nl, ws_d, (unsigned)rows, (unsigned)n_heads, total_tokens,
                      (float)(1.0 / (double)scale));
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)grid), dim3(kThreads), kDkvLds, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws_nl, ws_d, (uint16_t*)dk,
-                     (uint16_t*)dv, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens,
-                     c, scale, (int)n_logical);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)grid), dim3(kThreads), kDqLds, st, (const uint16_t*)q,
+  hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)(2 * grid)), dim3(kThreads), kDkvLds, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws_nl, ws_d, (uint16_t*)dq,
-                     cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, scale,
-                     (int)n_logical);
+                     (uint16_t*)dk, (uint16_t*)dv, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen,
+                     (int)n_heads, total_tokens, c, scale, (int)n_logical);
   if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
   return LSV_OK;
 }

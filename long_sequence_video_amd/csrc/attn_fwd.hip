@@ -710,13 +710,16 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ q, const u
   }
 }
 
+// The fused-Q forward, with the tail kernel's mapping: n_tail = 0 (lsv_attn_fwd_qnorm) runs every
+// tile whole, in the plain launch's XCDs and order.
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_qnorm_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                       uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                       int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
-                      int n_logical, QNorm qn) {
-  fwd_body<false, true>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c,
-                        n_logical, 1, nullptr, nullptr, qn);
+                      int n_logical, QNorm qn, int n_tail, int n_split, float* __restrict__ part_o,
+                      float* __restrict__ part_lse) {
+  fwd_body<false, true, true>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens,
+                              c, n_logical, n_split, part_o, part_lse, qn, n_tail);
 }
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -911,6 +914,27 @@ int fwd_checks(const void* q, const void* k, const void* v, const void* o, const
   return kProceed;
 }
 
+// lsv_attn_fwd_qnorm's checks beyond the forward's: a status to return, or kProceed with the tiles
+// per segment and the Q-side prologue's parameters.
+int qnorm_checks(const void* q, const void* k, const void* v, const void* q_weight, const void* cos, const void* sin,
+                 int32_t rotary_dim, float eps, const void* o, const float* lse, const int32_t* cu_seqlens,
+                 int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                 float scale, int64_t* tiles, QNorm* qn) {
+  if (!(eps >= 0.f) || !isfinite(eps)) return LSV_ERR_INVALID_ARG;
+  if (rotary_dim < 0 || rotary_dim > kD || rotary_dim % 16 != 0) return LSV_ERR_UNSUPPORTED;
+  const int rc = fwd_checks(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
+                            tiles);
+  if (rc != kProceed) return rc;
+  if (!q_weight || (rotary_dim > 0 && (!cos || !sin))) return LSV_ERR_INVALID_ARG;
+  if (((uintptr_t)q_weight | (uintptr_t)cos | (uintptr_t)sin) & 15) return LSV_ERR_ALIGNMENT;
+  qn->w = (const uint16_t*)q_weight;
+  qn->cos = (const uint16_t*)cos;
+  qn->sin = (const uint16_t*)sin;
+  qn->r = rotary_dim;
+  qn->eps = eps;
+  return kProceed;
+}
+
 }  // namespace
 
 extern "C" {
@@ -974,31 +998,66 @@ int lsv_attn_fwd_qnorm(const void* q, const void* k, const void* v, const void* 
                        const void* sin, int32_t rotary_dim, float eps, void* o, float* lse,
                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens,
                        int32_t n_heads, int32_t head_dim, float scale, void* stream) {
-  if (!(eps >= 0.f) || !isfinite(eps)) return LSV_ERR_INVALID_ARG;
-  if (rotary_dim < 0 || rotary_dim > kD || rotary_dim % 16 != 0) return LSV_ERR_UNSUPPORTED;
   int64_t tiles = 0;
-  const int rc = fwd_checks(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, n_heads, head_dim, scale,
-                            &tiles);
+  QNorm qn;
+  const int rc = qnorm_checks(q, k, v, q_weight, cos, sin, rotary_dim, eps, o, lse, cu_seqlens, n_seqs, max_seqlen,
+                              total_tokens, n_heads, head_dim, scale, &tiles, &qn);
   if (rc != kProceed) return rc;
-  if (!q_weight || (rotary_dim > 0 && (!cos || !sin))) return LSV_ERR_INVALID_ARG;
-  if (((uintptr_t)q_weight | (uintptr_t)cos | (uintptr_t)sin) & 15) return LSV_ERR_ALIGNMENT;
   const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
   const int64_t grid = (n_logical + 7) / 8 * 8;
   if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
   if (hipFuncSetAttribute((const void*)attn_fwd_qnorm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kLdsBytes) != hipSuccess)
     return LSV_ERR_HIP;
-  QNorm qn;
-  qn.w = (const uint16_t*)q_weight;
-  qn.cos = (const uint16_t*)cos;
-  qn.sin = (const uint16_t*)sin;
-  qn.r = rotary_dim;
-  qn.eps = eps;
   const float c = (float)((double)scale * 1.4426950408889634074);
   (void)hipGetLastError();
   hipLaunchKernelGGL(attn_fwd_qnorm_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, (hipStream_t)stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens,
-                     (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical, qn);
+                     (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical, qn, 0,
+                     1, (float*)nullptr, (float*)nullptr);
+  if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
+  return LSV_OK;
+}
+
+int lsv_attn_fwd_qnorm_tail(const void* q, const void* k, const void* v, const void* q_weight, const void* cos,
+                            const void* sin, int32_t rotary_dim, float eps, void* o, float* lse,
+                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int64_t total_tokens,
+                            int32_t n_heads, int32_t head_dim, float scale, int32_t compute_units, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  if (compute_units < 8 || compute_units % 8 != 0) return LSV_ERR_INVALID_ARG;
+  int64_t tiles = 0;
+  QNorm qn;
+  const int rc = qnorm_checks(q, k, v, q_weight, cos, sin, rotary_dim, eps, o, lse, cu_seqlens, n_seqs, max_seqlen,
+                              total_tokens, n_heads, head_dim, scale, &tiles, &qn);
+  if (rc != kProceed) return rc;
+  const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
+  int32_t n_split = 1;
+  int64_t n_tail = 0;
+  tail_plan(n_logical, max_seqlen, compute_units, &n_split, &n_tail);
+  if (n_split == 1)
+    return lsv_attn_fwd_qnorm(q, k, v, q_weight, cos, sin, rotary_dim, eps, o, lse, cu_seqlens, n_seqs, max_seqlen,
+                              total_tokens, n_heads, head_dim, scale, stream);
+  if (!workspace) return LSV_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 15) return LSV_ERR_ALIGNMENT;
+  const int64_t pieces = n_tail * n_split;
+  if (workspace_bytes < pieces * kBQ * (kD + 1) * (int64_t)sizeof(float)) return LSV_ERR_INVALID_ARG;
+  const int64_t grid = (n_logical + 7) / 8 * 8 - n_tail + pieces;  // 8 x (blocks per XCD)
+  if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute((const void*)attn_fwd_qnorm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return LSV_ERR_HIP;
+  float* part_o = (float*)workspace;
+  float* part_lse = part_o + pieces * kBQ * kD;
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  const hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attn_fwd_qnorm_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, cu_seqlens, (int)n_seqs, (int)tiles,
+                     (int)max_seqlen, (int)n_heads, total_tokens, c, (int)n_logical, qn, (int)n_tail, (int)n_split,
+                     part_o, part_lse);
+  hipLaunchKernelGGL(attn_fwd_tail_combine_kernel, dim3((unsigned)n_tail), dim3(256), 0, st, part_o, part_lse,
+                     (uint16_t*)o, lse, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads,
+                     total_tokens, (int)n_logical, (int)n_tail, (int)n_split);
   if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
   return LSV_OK;
 }

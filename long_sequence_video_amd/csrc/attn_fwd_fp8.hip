@@ -408,15 +408,51 @@ __device__ __forceinline__ void run(const Ctx& cx, int n_kt, Acc& acc, const i32
   wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS past this point
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
-                    uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
-                    int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
-                    float dv, int n_logical) {
+// Keys per range when a segment of seg_len keys is cut into n_split consecutive ranges: whole
+// 64-key tiles but for the last range; ranges that start at or past seg_len are empty.
+__device__ __forceinline__ int keys_per_split(int seg_len, int n_split) {
+  return ((seg_len + n_split - 1) / n_split + kBK - 1) / kBK * kBK;
+}
+
+// One workgroup: 256 query rows of one (segment, head) against all keys of the segment; O (bf16)
+// and the LSE are written.
+//
+// With kTail (lsv_attn_fwd_fp8_tail): XCD x owns logical tiles [x P, (x + 1) P), P =
+// ceil(n_logical / 8), as in the plain mapping (tiles from n_logical on do not exist). Its first
+// P - n_tail / 8 tiles run whole, in the same order; its last n_tail / 8 tiles (its last,
+// partial round) are cut into n_split key ranges that run after them on the same XCD. Tail tile
+// i = x (n_tail / 8) + r and range s form piece s n_tail + i, which writes its range's
+// dequantised, normalised fp32 O and its LSE to row (256 piece + row in tile) of the partial
+// buffers.
+template <bool kTail>
+__device__ __forceinline__ void fp8_body(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                                         const uint8_t* __restrict__ v, uint16_t* __restrict__ o,
+                                         float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens, int n_seqs,
+                                         int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
+                                         float dv, int n_logical, int n_tail, int n_split, float* __restrict__ part_o,
+                                         float* __restrict__ part_lse) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   // XCD-aware order, as in the BF16 kernel: head-major ranges per XCD.
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  int logical, split = 0, piece = -1;
+  if (kTail) {
+    const int xcd = blockIdx.x & 7;
+    const int j = blockIdx.x >> 3;  // this block's place in its XCD's sequence
+    const int per_xcd = (n_logical + 7) >> 3;
+    const int t = n_tail >> 3;
+    if (j < per_xcd - t) {
+      logical = xcd * per_xcd + j;
+    } else {
+      const int jt = j - (per_xcd - t);
+      if (jt >= t * n_split) return;
+      split = jt / t;
+      const int r = jt - split * t;
+      logical = xcd * per_xcd + per_xcd - t + r;
+      piece = split * n_tail + xcd * t + r;
+    }
+  } else {
+    const int per_xcd = gridDim.x >> 3;
+    logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  }
   if (logical >= n_logical) return;
   const int qt = logical % tiles_per_seq;
   const int hs = logical / tiles_per_seq;
@@ -429,6 +465,31 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   if (seg_len > max_seqlen) return;
   const int q0 = qt * kBQ;
   if (q0 >= seg_len) return;
+  int k0 = 0, k_len = seg_len;  // this workgroup's keys: [k0, k0 + k_len) of the segment
+  if (kTail && piece >= 0) {
+    const int per = keys_per_split(seg_len, n_split);
+    k0 = split * per;
+    k_len = min(per, seg_len - k0);
+    if (k_len <= 0) return;  // an empty range: the combine pass leaves it out
+  }
+  // Tail launches fix their epilogue destinations here, so that two addresses and a stride stay
+  // live through the key loop rather than the output and partial buffers and the indices into
+  // them. Row q0 + rr of the tile: O at o_dst + rr * o_stride, LSE at l_dst[rr].
+  char* o_dst = nullptr;
+  float* l_dst = nullptr;
+  int o_stride = 0;
+  if (kTail) {
+    const int64_t tok0 = (int64_t)seg_start + q0;
+    if (piece >= 0) {  // [piece][row in tile][d] and [piece][row in tile]
+      o_dst = (char*)(part_o + (int64_t)piece * kBQ * kD);
+      o_stride = kD * (int)sizeof(float);
+      l_dst = part_lse + (int64_t)piece * kBQ;
+    } else {  // the output itself
+      o_dst = (char*)(o + (tok0 * n_heads + head) * kD);
+      o_stride = n_heads * kD * (int)sizeof(uint16_t);
+      l_dst = lse + (int64_t)head * total_tokens + tok0;
+    }
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -436,18 +497,18 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   Ctx cx;
   cx.lds_copy = lds_base + wave * 1024;
   cx.row_stride = (unsigned)n_heads * kRow8;
-  cx.kbase = (const char*)k + ((int64_t)seg_start * n_heads + head) * kRow8;
-  cx.vbase = (const char*)v + ((int64_t)seg_start * n_heads + head) * kRow8;
+  cx.kbase = (const char*)k + ((int64_t)(seg_start + k0) * n_heads + head) * kRow8;
+  cx.vbase = (const char*)v + ((int64_t)(seg_start + k0) * n_heads + head) * kRow8;
   {
     const int i = tid & 63;
     cx.crow = 8 * wave + (i >> 3);
     cx.coff = (unsigned)(((i & 7) ^ sw8(cx.crow)) * 16);
     cx.cconst = (unsigned)cx.crow * cx.row_stride + cx.coff;
   }
-  cx.seg_len = seg_len;
+  cx.seg_len = k_len;  // the key loop sees only this workgroup's key range
   cx.c = c;
   cx.lazy = kLazyLog2 / c;
-  const int n_kt = (seg_len + kBK - 1) / kBK;
+  const int n_kt = (k_len + kBK - 1) / kBK;
 
   Lane ln;
   ln.lane = tid & 63;
@@ -509,38 +570,149 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   Acc acc;
   run(cx, n_kt, acc, qr, ln, sel);
 
-  // O = dv (P V) / sum(P) -> bf16; LSE = (m c - 5 + log2 l) ln 2.
+  // O = dv (P V) / sum(P) -> bf16; LSE = (m c - 5 + log2 l) ln 2. A key range (a tail piece)
+  // writes its O in fp32 and its LSE into the partial buffers.
   const float l = pair_sum(acc.l);
   const float lb = pair_sum(acc.LB[0]);  // lanes 32..63 hold 0
   const float mul = dv / lb;
   const int row = q0 + wave * 32 + ln.l32;
   if (row < seg_len) {
-    const int64_t tok = (int64_t)seg_start + row;
-    uint16_t* orow = o + (tok * n_heads + head) * kD;
+    if (kTail && piece >= 0) {
+      const int rr = row - q0;
+      float* prow = (float*)(o_dst + (int64_t)rr * o_stride);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x2 lo, hi;
-        lo[0] = (__bf16)(acc.O[db][4 * g + 0] * mul);
-        lo[1] = (__bf16)(acc.O[db][4 * g + 1] * mul);
-        hi[0] = (__bf16)(acc.O[db][4 * g + 2] * mul);
-        hi[1] = (__bf16)(acc.O[db][4 * g + 3] * mul);
-        u32x2 pk;
-        pk[0] = __builtin_bit_cast(unsigned, lo);
-        pk[1] = __builtin_bit_cast(unsigned, hi);
-        *(u32x2*)(orow + 32 * db + 8 * g + 4 * ln.h32) = pk;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = acc.O[db][4 * g + e] * mul;
+          *(f32x4*)(prow + 32 * db + 8 * g + 4 * ln.h32) = w;
+        }
+      if (ln.h32 == 0) l_dst[rr] = (acc.m * c - kRefLog2 + __log2f(l)) * 0.69314718055994530942f;
+    } else {
+      uint16_t* orow;
+      float* lrow;
+      if (kTail) {
+        orow = (uint16_t*)(o_dst + (int64_t)(row - q0) * o_stride);
+        lrow = l_dst + (row - q0);
+      } else {
+        const int64_t tok = (int64_t)seg_start + row;
+        orow = o + (tok * n_heads + head) * kD;
+        lrow = lse + (int64_t)head * total_tokens + tok;
       }
-    if (ln.h32 == 0) lse[(int64_t)head * total_tokens + tok] = (acc.m * c - kRefLog2 + __log2f(l)) * 0.69314718055994530942f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x2 lo, hi;
+          lo[0] = (__bf16)(acc.O[db][4 * g + 0] * mul);
+          lo[1] = (__bf16)(acc.O[db][4 * g + 1] * mul);
+          hi[0] = (__bf16)(acc.O[db][4 * g + 2] * mul);
+          hi[1] = (__bf16)(acc.O[db][4 * g + 3] * mul);
+          u32x2 pk;
+          pk[0] = __builtin_bit_cast(unsigned, lo);
+          pk[1] = __builtin_bit_cast(unsigned, hi);
+          *(u32x2*)(orow + 32 * db + 8 * g + 4 * ln.h32) = pk;
+        }
+      if (ln.h32 == 0) *lrow = (acc.m * c - kRefLog2 + __log2f(l)) * 0.69314718055994530942f;
+    }
   }
 }
 
-}  // namespace
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                    uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                    int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
+                    float dv, int n_logical) {
+  fp8_body<false>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c, dv,
+                  n_logical, 0, 1, nullptr, nullptr);
+}
 
-extern "C" int lsv_attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k,
-                                float descale_v, void* o, float* lse, const int32_t* cu_seqlens, int32_t n_seqs,
-                                int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
-                                float scale, void* stream) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_fp8_tail_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                         uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                         int n_seqs, int tiles_per_seq, int max_seqlen, int n_heads, int64_t total_tokens, float c,
+                         float dv, int n_logical, int n_tail, int n_split, float* __restrict__ part_o,
+                         float* __restrict__ part_lse) {
+  fp8_body<true>(q, k, v, o, lse, cu_seqlens, n_seqs, tiles_per_seq, max_seqlen, n_heads, total_tokens, c, dv,
+                 n_logical, n_tail, n_split, part_o, part_lse);
+}
+
+// Merges the key ranges of the tail tiles of attn_fwd_fp8_tail_kernel: block i takes tail tile
+// i = x (n_tail / 8) + r, the logical tile x P + P - n_tail / 8 + r (P = ceil(n_logical / 8);
+// none from n_logical on), with the forward's segment checks; per row, over the non-empty ranges
+// r, LSE = ln sum_r exp(LSE_r) and O = sum_r exp(LSE_r - LSE) O_r in fp32, then bf16 (nearest
+// even). 16 lanes per row, 8 dims a lane.
+__global__ void __launch_bounds__(256)
+attn_fwd_fp8_tail_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                 uint16_t* __restrict__ o, float* __restrict__ lse,
+                                 const int32_t* __restrict__ cu_seqlens, int n_seqs, int tiles_per_seq,
+                                 int max_seqlen, int n_heads, int64_t total_tokens, int n_logical, int n_tail,
+                                 int n_split) {
+  const int t = blockIdx.x;
+  if (t >= n_tail) return;
+  const int per_xcd = (n_logical + 7) >> 3;
+  const int tail_per_xcd = n_tail >> 3;
+  const int logical = (t / tail_per_xcd + 1) * per_xcd - tail_per_xcd + t % tail_per_xcd;
+  if (logical >= n_logical) return;  // past the end of the last XCD's range
+  const int qt = logical % tiles_per_seq;
+  const int hs = logical / tiles_per_seq;
+  const int seg = hs % n_seqs;
+  const int head = hs / n_seqs;
+  const int seg_start = cu_seqlens[seg];
+  const int seg_end = cu_seqlens[seg + 1];
+  if (seg_start < 0 || seg_end < seg_start || (int64_t)seg_end > total_tokens) return;
+  const int seg_len = seg_end - seg_start;
+  if (seg_len > max_seqlen) return;
+  const int q0 = qt * kBQ;
+  if (q0 >= seg_len) return;
+  const int per = keys_per_split(seg_len, n_split);
+  const int n_ranges = (seg_len + per - 1) / per;  // the non-empty ranges
+  const int j = threadIdx.x & 15;
+  const int q_end = min(q0 + kBQ, seg_len);
+  for (int row = q0 + (threadIdx.x >> 4); row < q_end; row += 16) {
+    const int64_t tok = (int64_t)seg_start + row;
+    float m = -INFINITY;
+    for (int r = 0; r < n_ranges; ++r) m = fmaxf(m, part_lse[(int64_t)(r * n_tail + t) * kBQ + (row - q0)]);
+    float sum = 0.f;
+    f32x4 a = {}, b = {};
+    for (int r = 0; r < n_ranges; ++r) {
+      const int64_t pr = (int64_t)(r * n_tail + t) * kBQ + (row - q0);
+      const float w = __expf(part_lse[pr] - m);
+      sum += w;
+      const f32x4* src = (const f32x4*)(part_o + pr * kD + 8 * j);
+      const f32x4 x = src[0], y = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = __builtin_fmaf(w, x[e], a[e]);
+        b[e] = __builtin_fmaf(w, y[e], b[e]);
+      }
+    }
+    const float inv = 1.f / sum;
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      bf16x2 lo, hi;
+      lo[0] = (__bf16)(a[2 * e] * inv);
+      lo[1] = (__bf16)(a[2 * e + 1] * inv);
+      hi[0] = (__bf16)(b[2 * e] * inv);
+      hi[1] = (__bf16)(b[2 * e + 1] * inv);
+      pk[e] = __builtin_bit_cast(unsigned, lo);
+      pk[2 + e] = __builtin_bit_cast(unsigned, hi);
+    }
+    *(u32x4*)(o + (tok * n_heads + head) * kD + 8 * j) = pk;
+    if (j == 0) lse[(int64_t)head * total_tokens + tok] = m + __logf(sum);
+  }
+}
+
+constexpr int kProceed = 1;  // fp8_checks: arguments valid and there is work to launch
+
+// The FP8 forward's argument checks (before any HIP call): a status to return, or kProceed with
+// the number of 256-row query tiles per segment and c = scale dq dk log2(e).
+int fp8_checks(const void* q, const void* k, const void* v, float descale_q, float descale_k, float descale_v,
+               const void* o, const float* lse, const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+               int64_t total_tokens, int32_t n_heads, int32_t head_dim, float scale, int64_t* tiles, float* c) {
   if (n_seqs < 0 || max_seqlen < 0 || total_tokens < 0 || n_heads < 1) return LSV_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return LSV_ERR_INVALID_ARG;
   if (!(descale_q > 0.f) || !(descale_k > 0.f) || !(descale_v > 0.f) || !isfinite(descale_q) ||
@@ -556,12 +728,26 @@ extern "C" int lsv_attn_fwd_fp8(const void* q, const void* k, const void* v, flo
   if (row_stride >= (1 << 24) || (int64_t)max_seqlen >= (1 << 24) ||
       (int64_t)max_seqlen * row_stride + kRow8 > (int64_t)UINT32_MAX)
     return LSV_ERR_UNSUPPORTED;
-  const int64_t tiles = ((int64_t)max_seqlen + kBQ - 1) / kBQ;
+  *tiles = ((int64_t)max_seqlen + kBQ - 1) / kBQ;
+  *c = (float)((double)scale * (double)descale_q * (double)descale_k * 1.4426950408889634074);
+  if (!(*c > 0.f) || !isfinite(*c)) return LSV_ERR_INVALID_ARG;
+  return kProceed;
+}
+
+}  // namespace
+
+extern "C" int lsv_attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                                float descale_v, void* o, float* lse, const int32_t* cu_seqlens, int32_t n_seqs,
+                                int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                                float scale, void* stream) {
+  int64_t tiles = 0;
+  float c = 0.f;
+  const int rc = fp8_checks(q, k, v, descale_q, descale_k, descale_v, o, lse, cu_seqlens, n_seqs, max_seqlen,
+                            total_tokens, n_heads, head_dim, scale, &tiles, &c);
+  if (rc != kProceed) return rc;
   const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
   const int64_t grid = (n_logical + 7) / 8 * 8;
   if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
-  const float c = (float)((double)scale * (double)descale_q * (double)descale_k * 1.4426950408889634074);
-  if (!(c > 0.f) || !isfinite(c)) return LSV_ERR_INVALID_ARG;
   if (hipFuncSetAttribute((const void*)attn_fwd_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kLdsBytes) != hipSuccess)
     return LSV_ERR_HIP;
@@ -570,6 +756,53 @@ extern "C" int lsv_attn_fwd_fp8(const void* q, const void* k, const void* v, flo
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, cu_seqlens,
                      (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, descale_v,
                      (int)n_logical);
+  if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
+  return LSV_OK;
+}
+
+// The plan (lsv_attn_fwd_tail_plan) counts 256-row query tiles and keeps at least 1024 keys per
+// range, i.e. whole 64-key tiles here.
+static_assert(kBQ == 256 && 1024 % kBK == 0, "the tail plan's tile and range sizes");
+
+extern "C" int lsv_attn_fwd_fp8_tail(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                                     float descale_v, void* o, float* lse, const int32_t* cu_seqlens, int32_t n_seqs,
+                                     int32_t max_seqlen, int64_t total_tokens, int32_t n_heads, int32_t head_dim,
+                                     float scale, int32_t compute_units, void* workspace, int64_t workspace_bytes,
+                                     void* stream) {
+  if (compute_units < 8 || compute_units % 8 != 0) return LSV_ERR_INVALID_ARG;
+  int64_t tiles = 0;
+  float c = 0.f;
+  const int rc = fp8_checks(q, k, v, descale_q, descale_k, descale_v, o, lse, cu_seqlens, n_seqs, max_seqlen,
+                            total_tokens, n_heads, head_dim, scale, &tiles, &c);
+  if (rc != kProceed) return rc;
+  int32_t n_split = 1;
+  int64_t n_tail = 0;
+  if (lsv_attn_fwd_tail_plan(n_seqs, max_seqlen, n_heads, compute_units, &n_split, &n_tail) != LSV_OK)
+    return LSV_ERR_INVALID_ARG;
+  if (n_split == 1)
+    return lsv_attn_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, o, lse, cu_seqlens, n_seqs, max_seqlen,
+                            total_tokens, n_heads, head_dim, scale, stream);
+  if (!workspace) return LSV_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 15) return LSV_ERR_ALIGNMENT;
+  const int64_t pieces = n_tail * n_split;
+  if (workspace_bytes < pieces * kBQ * (kD + 1) * (int64_t)sizeof(float)) return LSV_ERR_INVALID_ARG;
+  const int64_t n_logical = tiles * n_seqs * (int64_t)n_heads;
+  const int64_t grid = (n_logical + 7) / 8 * 8 - n_tail + pieces;  // 8 x (blocks per XCD)
+  if (grid > (int64_t)INT32_MAX) return LSV_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute((const void*)attn_fwd_fp8_tail_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return LSV_ERR_HIP;
+  float* part_o = (float*)workspace;
+  float* part_lse = part_o + pieces * kBQ * kD;
+  const hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attn_fwd_fp8_tail_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, st,
+                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, cu_seqlens,
+                     (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads, total_tokens, c, descale_v,
+                     (int)n_logical, (int)n_tail, (int)n_split, part_o, part_lse);
+  hipLaunchKernelGGL(attn_fwd_fp8_tail_combine_kernel, dim3((unsigned)n_tail), dim3(256), 0, st, part_o, part_lse,
+                     (uint16_t*)o, lse, cu_seqlens, (int)n_seqs, (int)tiles, (int)max_seqlen, (int)n_heads,
+                     total_tokens, (int)n_logical, (int)n_tail, (int)n_split);
   if (hipGetLastError() != hipSuccess) return LSV_ERR_LAUNCH;
   return LSV_OK;
 }

@@ -81,3 +81,28 @@ def compare(inp, out_bits, lse, rows=None, *, label=""):
     assert stats["o_mean"] <= O_MEAN_ABS, stats
     assert stats["lse_max"] <= LSE_MAX_ABS, stats
     return stats
+
+
+def tail_tiles(inp, units):
+    """The plan's (split, tail logical tiles): XCD x owns logical tiles [x P, (x + 1) P),
+    P = ceil(n / 8) (none from n on), and its last n_tail / 8 are the cut ones."""
+    import long_sequence_video_amd as lsv
+    split, n_tail = lsv.lsv_attn_fwd_tail_plan(len(inp.cu_seqlens) - 1, inp.max_seqlen, inp.n_heads, units)
+    n = (inp.max_seqlen + 255) // 256 * (len(inp.cu_seqlens) - 1) * inp.n_heads
+    per_xcd, t = -(-n // 8), n_tail // 8
+    return split, [x * per_xcd + per_xcd - t + r for x in range(8) for r in range(t)
+                   if x * per_xcd + per_xcd - t + r < n]
+
+
+def whole_tile_rows(inp, units):
+    """(token, head) pairs of the query tiles that the plan leaves whole, as a boolean [T, H]."""
+    split, tail = tail_tiles(inp, units)
+    tiles = (inp.max_seqlen + 255) // 256
+    n_seqs = len(inp.cu_seqlens) - 1
+    whole = np.ones((inp.total_tokens, inp.n_heads), bool)
+    for logical in tail:
+        qt, hs = logical % tiles, logical // tiles
+        seg, head = hs % n_seqs, hs // n_seqs
+        a, b = int(inp.cu_seqlens[seg]), int(inp.cu_seqlens[seg + 1])
+        whole[a + 256 * qt:min(b, a + 256 * qt + 256), head] = False
+    return whole, split, len(tail)

@@ -389,3 +389,70 @@ def test_tail_validation_before_any_hip_call(args, code):
                                a["total_tokens"], a["n_heads"], a["head_dim"], a["scale"], a["units"], a["ws"],
                                a["ws_bytes"], None)
     assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(units=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(units=100), lsv.LSV_ERR_INVALID_ARG),
+    (dict(ws=0), lsv.LSV_ERR_INVALID_ARG),             # this plan cuts 6 ranges: a workspace is needed
+    (dict(ws=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(ws_bytes=40 * 6 * 256 * 129 * 4 - 1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(dq=0.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dv=float("nan")), lsv.LSV_ERR_INVALID_ARG),
+    (dict(dq=1e30, dk=1e30), lsv.LSV_ERR_INVALID_ARG),     # scale * dq * dk overflows fp32
+    (dict(q=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(k=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(max_seqlen=599_187, total_tokens=599_187, n_heads=56), lsv.LSV_ERR_UNSUPPORTED),  # 32-bit offsets
+    (dict(n_seqs=0, ws=0), lsv.LSV_OK),
+])
+def test_fp8_tail_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, dq=0.01, dk=0.01, dv=0.01, n_seqs=1, max_seqlen=19394,
+             total_tokens=19394, n_heads=14, head_dim=128, scale=0.125, units=256, ws=A,
+             ws_bytes=40 * 6 * 256 * 129 * 4)
+    a.update(args)
+    rc = lsv.lsv_attn_fwd_fp8_tail(a["q"], a["k"], a["v"], a["dq"], a["dk"], a["dv"], a["o"], a["lse"], a["cu"],
+                                   a["n_seqs"], a["max_seqlen"], a["total_tokens"], a["n_heads"], a["head_dim"],
+                                   a["scale"], a["units"], a["ws"], a["ws_bytes"], None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(units=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(units=100), lsv.LSV_ERR_INVALID_ARG),
+    (dict(ws=0), lsv.LSV_ERR_INVALID_ARG),             # this plan cuts 6 ranges: a workspace is needed
+    (dict(ws=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(ws_bytes=40 * 6 * 256 * 129 * 4 - 1), lsv.LSV_ERR_INVALID_ARG),
+    (dict(rotary_dim=8), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(head_dim=64), lsv.LSV_ERR_UNSUPPORTED),
+    (dict(w=0), lsv.LSV_ERR_INVALID_ARG),
+    (dict(sin=A + 8), lsv.LSV_ERR_ALIGNMENT),
+    (dict(n_seqs=0, ws=0), lsv.LSV_OK),
+])
+def test_attn_fwd_qnorm_tail_validation_before_any_hip_call(args, code):
+    a = dict(q=A, k=A, v=A, w=A, cos=A, sin=A, rotary_dim=96, eps=1e-5, o=A, lse=A, cu=A, n_seqs=1,
+             max_seqlen=19394, total_tokens=19394, n_heads=14, head_dim=128, scale=0.125, units=256, ws=A,
+             ws_bytes=40 * 6 * 256 * 129 * 4)
+    a.update(args)
+    rc = lsv.lsv_attn_fwd_qnorm_tail(a["q"], a["k"], a["v"], a["w"], a["cos"], a["sin"], a["rotary_dim"], a["eps"],
+                                     a["o"], a["lse"], a["cu"], a["n_seqs"], a["max_seqlen"], a["total_tokens"],
+                                     a["n_heads"], a["head_dim"], a["scale"], a["units"], a["ws"], a["ws_bytes"],
+                                     None)
+    assert rc == code
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before torch is imported must not map a second HIP runtime: torch ships
+    its own, and kernels registered with one runtime cannot run on the other's streams or memory
+    (a fresh process, so nothing has imported torch yet)."""
+    import subprocess
+    import sys
+    code = ("import long_sequence_video_amd as lsv\n"
+            "lsv.load_library()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout

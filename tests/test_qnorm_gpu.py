@@ -8,6 +8,8 @@
 * ``lsv_attn_fwd_qnorm`` bit-identical to the two-pass path ``lsv_norm_rope(q)`` then
   ``lsv_attn_fwd`` (it computes Q with the prologue's exact fp32 steps and summation order), on
   every rotary width the prologue supports.
+* ``lsv_attn_fwd_qnorm_tail`` (the launch that cuts the last, partial round of query tiles into
+  key ranges) bit-identical to ``lsv_norm_rope(q)`` then ``lsv_attn_fwd_tail`` with the same plan.
 * ``lsv_attn_fwd_qnorm`` against the oracle composition: the prologue oracle's exact Q and K
   rounded to bf16, then the attention oracle, at the forward's tolerances (O max-abs 2e-2,
   mean-abs 2e-3, LSE 1e-3); every row of ragged packs, sampled rows of the 161,394-token pack
@@ -74,9 +76,10 @@ def test_norm_rope_every_element_and_equal_to_the_qkv_prologue(gpu, rotary_dim):
     assert np.array_equal(st[0], from_dev(lsv.norm_rope(q, qw, cos, sin, eps=inp.eps)))
 
 
-def _fused_and_two_pass(inp, device, max_seqlen=None):
-    """(O, LSE) of lsv_attn_fwd_qnorm and of lsv_norm_rope(q) -> lsv_attn_fwd, on the same k, v;
-    k is the prologue oracle's K rounded to bf16."""
+def _fused_and_two_pass(inp, device, max_seqlen=None, units=None):
+    """(O, LSE) of lsv_attn_fwd_qnorm and of lsv_norm_rope(q) -> lsv_attn_fwd, on the same k, v
+    (with ``units``: lsv_attn_fwd_qnorm_tail and lsv_norm_rope(q) -> lsv_attn_fwd_tail on that many
+    compute units); k is the prologue oracle's K rounded to bf16."""
     import torch
     import long_sequence_video_amd as lsv
     kref, _ = _oracle_rows(inp.k, inp.k_weight, inp.cos, inp.sin, inp.eps)
@@ -86,9 +89,12 @@ def _fused_and_two_pass(inp, device, max_seqlen=None):
     cos, sin = _dev_tables(inp, device)
     cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device)
     ms = inp.max_seqlen if max_seqlen is None else max_seqlen
-    o1, l1 = lsv.attn_fwd_qnorm(q, k, v, qw, cos, sin, cu, ms, inp.scale, eps=inp.eps)
+    o1, l1 = lsv.attn_fwd_qnorm(q, k, v, qw, cos, sin, cu, ms, inp.scale, eps=inp.eps, compute_units=units)
     qn = lsv.norm_rope(q, qw, cos, sin, eps=inp.eps)
-    o2, l2 = lsv.attn_fwd(qn, k, v, cu, ms, inp.scale)
+    if units is None:
+        o2, l2 = lsv.attn_fwd(qn, k, v, cu, ms, inp.scale)
+    else:
+        o2, l2 = lsv.attn_fwd_tail(qn, k, v, cu, ms, inp.scale, compute_units=units)
     torch.cuda.synchronize(device)
     return (from_dev(o1), l1.cpu().numpy()), (from_dev(o2), l2.cpu().numpy()), k_bits
 
@@ -108,6 +114,32 @@ def test_fused_equals_two_pass_and_matches_the_oracle(gpu, seqlens, heads, rotar
     (o1, l1), (o2, l2), k_bits = _fused_and_two_pass(inp, gpu)
     assert np.array_equal(o1, o2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
     compare(_composition(inp, k_bits), o1, l1, label=f"qnorm {seqlens} h{heads} R={rotary_dim}")
+
+
+@pytest.mark.parametrize("rotary_dim", [0, 96])
+@pytest.mark.parametrize("seqlens,heads,units", [
+    ([5000], 8, 128),            # 20 tiles per XCD: the last 4 cut into 4 ranges
+    ([9000, 300, 4097], 2, 96),  # 27 per XCD: 24 tail tiles, 12 of them empty, 4 ranges
+    ([4104], 7, 96),             # 119 tiles, 15 per XCD: the last 3 cut; XCD 7's last one does not exist
+])
+def test_fused_tail_equals_two_pass_tail_and_matches_the_oracle(gpu, seqlens, heads, units, rotary_dim):
+    """lsv_attn_fwd_qnorm_tail bit-identical to lsv_norm_rope(q) -> lsv_attn_fwd_tail with the same
+    plan (the cut tiles included), whole tiles bit-identical to lsv_attn_fwd_qnorm, and every row
+    against the oracle composition."""
+    from tests.gpu_common import whole_tile_rows
+    # RoPE tables, as in the other oracle comparisons of the fused forward: the oracle composition
+    # rounds its exact Q to bf16 on its own, and random N(0,1) tables scale Q so far that one ulp
+    # of it moves a score by centinats
+    inp = gen.generate_qnorm(seqlens, heads, rotary_dim, seed=97 + units + rotary_dim)
+    whole, split, n_tail = whole_tile_rows(inp, units)
+    assert split > 1 and n_tail > 0
+    say(f"case attn_fwd_qnorm_tail {seqlens} h{heads} units {units} R={rotary_dim}: {n_tail} x {split}")
+    (o1, l1), (o2, l2), k_bits = _fused_and_two_pass(inp, gpu, units=units)
+    assert np.array_equal(o1, o2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+    (o3, l3), _, _ = _fused_and_two_pass(inp, gpu)
+    assert np.array_equal(o1[whole], o3[whole])
+    assert np.array_equal(l1.T[whole].view(np.uint32), l3.T[whole].view(np.uint32))
+    compare(_composition(inp, k_bits), o1, l1, label=f"qnorm tail {seqlens} h{heads} units {units}")
 
 
 def test_fused_rows_outside_segments_untouched(gpu):
@@ -141,10 +173,24 @@ def test_fused_varlen_pack_sampled(gpu):
     (o1, l1), (o2, l2), k_bits = _fused_and_two_pass(inp, gpu)
     assert np.array_equal(o1, o2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
     del o2, l2
+    # the launch the benchmark times (the device's plan: 24 tail tiles x 8 ranges)
+    import long_sequence_video_amd as lsv
+    units = lsv.lsv_device_peak(0)[1]
+    (o4, l4), (o5, l5), _ = _fused_and_two_pass(inp, gpu, units=units)
+    assert np.array_equal(o4, o5) and np.array_equal(l4.view(np.uint32), l5.view(np.uint32))
+    del o5, l5
     rows = sample_rows(inp, 24, seed=8)
     qref, _ = _oracle_rows(inp.q[rows], inp.q_weight, inp.cos[rows], inp.sin[rows], inp.eps)
     q_bits = np.zeros_like(inp.q)
     q_bits[rows] = gen.f64_to_bf16_bits(qref)
     comp = gen.Inputs(inp.name, q_bits, k_bits, inp.v, inp.cu_seqlens, inp.scale)
     compare(comp, o1, l1, rows=rows, label="qnorm varlen pack")
+    from tests.gpu_common import whole_tile_rows
+    whole, _, _ = whole_tile_rows(inp, units)
+    cut = np.flatnonzero(~whole.all(axis=1))
+    if len(cut):
+        qref, _ = _oracle_rows(inp.q[cut], inp.q_weight, inp.cos[cut], inp.sin[cut], inp.eps)
+        q_bits[cut] = gen.f64_to_bf16_bits(qref)
+        comp = gen.Inputs(inp.name, q_bits, k_bits, inp.v, inp.cu_seqlens, inp.scale)
+        compare(comp, o4, l4, rows=np.union1d(cut, rows), label="qnorm tail varlen pack")
     torch.cuda.empty_cache()

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from long_sequence_video_amd import inputs as gen
-from tests.gpu_common import compare, from_dev, sample_rows, say, to_dev
+from tests.gpu_common import compare, from_dev, sample_rows, say, to_dev, whole_tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -33,31 +33,6 @@ def run_tail(inp, device, units=None, *, out_fill=None):
     ref_o, ref_l = lsv.attn_fwd(q, k, v, cu, inp.max_seqlen, inp.scale)
     torch.cuda.synchronize(device)
     return from_dev(out), lse.cpu().numpy(), from_dev(ref_o), ref_l.cpu().numpy()
-
-
-def tail_tiles(inp, units):
-    """The plan's (split, tail logical tiles): XCD x owns logical tiles [x P, (x + 1) P),
-    P = ceil(n / 8) (none from n on), and its last n_tail / 8 are the cut ones."""
-    import long_sequence_video_amd as lsv
-    split, n_tail = lsv.lsv_attn_fwd_tail_plan(len(inp.cu_seqlens) - 1, inp.max_seqlen, inp.n_heads, units)
-    n = (inp.max_seqlen + 255) // 256 * (len(inp.cu_seqlens) - 1) * inp.n_heads
-    per_xcd, t = -(-n // 8), n_tail // 8
-    return split, [x * per_xcd + per_xcd - t + r for x in range(8) for r in range(t)
-                   if x * per_xcd + per_xcd - t + r < n]
-
-
-def whole_tile_rows(inp, units):
-    """(token, head) pairs of the query tiles that the plan leaves whole, as a boolean [T, H]."""
-    split, tail = tail_tiles(inp, units)
-    tiles = (inp.max_seqlen + 255) // 256
-    n_seqs = len(inp.cu_seqlens) - 1
-    whole = np.ones((inp.total_tokens, inp.n_heads), bool)
-    for logical in tail:
-        qt, hs = logical % tiles, logical // tiles
-        seg, head = hs % n_seqs, hs // n_seqs
-        a, b = int(inp.cu_seqlens[seg]), int(inp.cu_seqlens[seg + 1])
-        whole[a + 256 * qt:min(b, a + 256 * qt + 256), head] = False
-    return whole, split, len(tail)
 
 
 @pytest.mark.parametrize("seqlens,heads,units", [

@@ -1,6 +1,6 @@
 """The backward's no-allocation entry point, lsv_attn_bwd_noalloc, against lsv_attn_bwd.
 
-Both run the same three kernels; the no-alloc one keeps the per-(head, token) statistics in
+Both run the same two kernels; the no-alloc one keeps the per-(head, token) statistics in
 the library's own device scratch instead of a caller's workspace. Two calls in a row, the
 second with a smaller input (the scratch keeps the first call's contents, which the second
 must overwrite where it reads): each must give gradients bit-identical to lsv_attn_bwd's on
