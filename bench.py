@@ -69,6 +69,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense BF16 MFMA peak (2.5 PFLOP/s)
 DEFAULT_CONFIG = "varlen_19394_38000_104000_h56"
 # The segment of the default pack that the 40% target is stated for, run alone.
 EXTRA_CONFIGS = {"h56_s104000": dict(seqlens=[104000], heads=56, seed=1005),
+                 # one sp=4 rank's 14-head share of the 38,000-token clip (RMS-normalised Q/K)
+                 "sp4_share_s38000_h14": dict(seqlens=[38000], heads=14, seed=1008, rms_qk=True),
                  # 38,000 x 56 with every query's first key tile ~113 nats below the rest: every
                  # workgroup's fixed-reference pass overflows and reruns on the exact path.
                  "fallback_s38000_h56": dict(seqlens=[38000], heads=56, seed=1004, rms_qk=True,
