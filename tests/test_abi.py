@@ -456,3 +456,31 @@ def test_library_shares_torchs_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+def test_tail_plan_invariants_over_random_sizes():
+    """lsv_attn_fwd_tail_plan against the contract its header states, on 3,000 seeded random sizes:
+    with n tiles and P = ceil(n / 8) per XCD of units / 8 slots, the cut tiles are the t = P mod
+    slots past the last whole round, cut only when 1 <= t <= slots / 4, into at most 8 ranges,
+    at most slots / t (so each XCD's pieces fill at most one round) and at most max_seqlen / 1024
+    (ranges of >= 1024 keys); the pieces fit the workspace lsv_attn_fwd_tail_workspace_size
+    promises; nothing is cut otherwise."""
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    for _ in range(3000):
+        n_seqs = int(rng.integers(1, 6))
+        max_seqlen = int(rng.choice([rng.integers(1, 4096), rng.integers(4096, 300_000)]))
+        heads = int(rng.integers(1, 65))
+        units = 8 * int(rng.integers(1, 41))
+        split, n_tail = lsv.lsv_attn_fwd_tail_plan(n_seqs, max_seqlen, heads, units)
+        n = -(-max_seqlen // 256) * n_seqs * heads
+        slots, t = units // 8, -(-n // 8) % (units // 8)
+        if split == 1:
+            assert n_tail == 0
+            assert t == 0 or t > slots // 4 or min(8, slots // t, max_seqlen // 1024) < 2
+            continue
+        assert n_tail == 8 * t and 1 <= t <= slots // 4
+        assert 2 <= split <= min(8, slots // t, max_seqlen // 1024)
+        assert split == min(8, slots // t, max_seqlen // 1024)
+        assert t * split <= slots
+        assert n_tail * split * 256 * 129 * 4 <= lsv.lsv_attn_fwd_tail_workspace_size(units)

@@ -218,7 +218,8 @@ def test_fp8_largest_supported_segment(gpu):
     """One segment of 599,186 tokens x 56 heads, the largest the FP8 kernel's 32-bit
     in-segment offsets allow (its e4m3 rows are 128 bytes: max_seqlen * heads * 128 + 128 < 2^32;
     one token more is rejected on the host). The first and last head (the lowest and highest
-    addresses) against the oracle on the first and last 32 query rows and 16 random ones."""
+    addresses) against the oracle on the first and last 32 query rows and 16 random ones; then the
+    tail launch on the same inputs."""
     import torch
     n = 599_186
     assert n * 56 * 128 + 128 < 2 ** 32 <= (n + 1) * 56 * 128 + 128
@@ -233,7 +234,30 @@ def test_fp8_largest_supported_segment(gpu):
     say("case fp8 max segment 599186 x 56: oracle")
     compare_fp8(sub, np.ascontiguousarray(out[:, hs]), np.ascontiguousarray(lse[hs]), rows=rows,
                 label="fp8 max segment 599186 x 56")
-    del f8, sub, out, lse
+    del sub
+    # The tail launch on the same inputs (the device's plan: the last tiles of one head per XCD,
+    # so the cut ranges start deep into the segment): whole tiles bit-identical to the plain
+    # launch, every row of the cut tiles on the cut heads against the oracle.
+    from tests.gpu_common import whole_tile_rows
+    from tests.test_fp8_tail_gpu import run_fp8_tail
+    import long_sequence_video_amd as lsv
+    whole, split, n_tail = whole_tile_rows(f8, lsv.lsv_device_peak(0)[1])
+    say(f"case fp8 max segment 599186 x 56: tail launch, {n_tail} tail tiles x {split} ranges")
+    out_t, lse_t, ref_o, ref_l = run_fp8_tail(f8, gpu)
+    assert np.array_equal(out_t[whole], ref_o[whole])
+    assert np.array_equal(lse_t.T[whole].view(np.uint32), ref_l.T[whole].view(np.uint32))
+    del ref_o, ref_l, out, lse
+    if n_tail:
+        cut_heads = [h for h in range(56) if not whole[:, h].all()]
+        cut_rows = np.flatnonzero(~whole.all(axis=1))
+        sub = gen.Fp8Inputs("fp8_max_segment_cut_heads",
+                            *(np.ascontiguousarray(x[:, cut_heads]) for x in (f8.q, f8.k, f8.v)),
+                            f8.descale_q, f8.descale_k, f8.descale_v, f8.cu_seqlens, f8.scale)
+        say(f"case fp8 max segment 599186 x 56: oracle on {len(cut_rows)} cut rows x {len(cut_heads)} heads")
+        compare_fp8(sub, np.ascontiguousarray(out_t[:, cut_heads]), np.ascontiguousarray(lse_t[cut_heads]),
+                    rows=cut_rows, label="fp8 tail max segment 599186 x 56")
+        del sub
+    del f8, out_t, lse_t
     torch.cuda.empty_cache()
 
 

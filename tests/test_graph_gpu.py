@@ -2,8 +2,10 @@
 
 One graph holds a forward step and a backward step the way a training or serving loop would
 capture them: the K-side prologue and the forward with Q's norm and rotation in its Q load
-(lsv_norm_rope, lsv_attn_fwd_qnorm), the tail-split forward (lsv_attn_fwd_tail), the backward
-that allocates nothing (lsv_attn_bwd_noalloc) and the FP8 forward (lsv_attn_fwd_fp8). Every
+(lsv_norm_rope, lsv_attn_fwd_qnorm, and lsv_attn_fwd_qnorm_tail), the tail-split forward
+(lsv_attn_fwd_tail), the backward that allocates nothing (lsv_attn_bwd_noalloc) and the FP8
+forward (lsv_attn_fwd_fp8, and lsv_attn_fwd_fp8_tail); the three tail launches share one
+workspace, which their order on the stream makes safe. Every
 buffer is allocated before capture and max_seqlen is passed, so nothing allocates, copies to
 the host or synchronises inside the capture. The graph is replayed several times, with other
 work and synchronisations between the replays, new inputs copied into the captured buffers in
@@ -51,12 +53,14 @@ class Buffers:
         self.sin = torch.empty_like(self.cos)
         self.q8, self.k8, self.v8 = (torch.empty((t, h, 128), dtype=torch.uint8, device=device) for _ in range(3))
         self.cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device)
-        self.kn, self.o_qn, self.o, self.o8 = bf(), bf(), bf(), bf()
+        self.kn, self.o_qn, self.o, self.o8, self.o_qt, self.o8t = bf(), bf(), bf(), bf(), bf(), bf()
         self.dq, self.dk, self.dv = bf(), bf(), bf()
-        self.l_qn, self.l, self.l8 = (torch.empty((h, t), dtype=torch.float32, device=device) for _ in range(3))
+        self.l_qn, self.l, self.l8, self.l_qt, self.l8t = (torch.empty((h, t), dtype=torch.float32, device=device)
+                                                           for _ in range(5))
         import long_sequence_video_amd as lsv
         self.ws = torch.empty(lsv.lsv_attn_fwd_tail_workspace_size(UNITS), dtype=torch.uint8, device=device)
-        self.outputs = (self.kn, self.o_qn, self.l_qn, self.o, self.l, self.dq, self.dk, self.dv, self.o8, self.l8)
+        self.outputs = (self.kn, self.o_qn, self.l_qn, self.o, self.l, self.dq, self.dk, self.dv, self.o8, self.l8,
+                        self.o_qt, self.l_qt, self.o8t, self.l8t)
 
     def load(self, inp, do, f8):
         import torch
@@ -88,6 +92,10 @@ def step(b, inp):
     lsv.attn_bwd_noalloc(b.q, b.k, b.v, b.o, b.do, b.l, b.cu, ms, inp.scale, dq=b.dq, dk=b.dk, dv=b.dv)
     lsv.attn_fwd_fp8(b.q8, b.k8, b.v8, b.f8.descale_q, b.f8.descale_k, b.f8.descale_v, b.cu, ms, b.f8.scale,
                      out=b.o8, lse=b.l8)
+    lsv.attn_fwd_qnorm(b.q, b.kn, b.v, b.qw, b.cos, b.sin, b.cu, ms, inp.scale, eps=inp.eps, out=b.o_qt, lse=b.l_qt,
+                       compute_units=UNITS, workspace=b.ws)
+    lsv.attn_fwd_fp8_tail(b.q8, b.k8, b.v8, b.f8.descale_q, b.f8.descale_k, b.f8.descale_v, b.cu, ms, b.f8.scale,
+                          compute_units=UNITS, out=b.o8t, lse=b.l8t, workspace=b.ws)
 
 
 def _same(a, b):
