@@ -1,5 +1,6 @@
-"""Shared helpers for the GPU parity tests: moving bf16 bit arrays to and from the device
-and comparing kernel outputs with the fp64 oracle at the stated tolerances."""
+"""Shared helpers for the GPU parity tests: moving bf16 bit arrays to and from the device,
+comparing kernel outputs with the fp64 oracle at the stated tolerances, the query tiles a tail
+plan cuts, and the FP8 tail launch beside the plain one."""
 
 from __future__ import annotations
 
@@ -106,3 +107,21 @@ def whole_tile_rows(inp, units):
         a, b = int(inp.cu_seqlens[seg]), int(inp.cu_seqlens[seg + 1])
         whole[a + 256 * qt:min(b, a + 256 * qt + 256), head] = False
     return whole, split, len(tail)
+
+
+def run_fp8_tail(f8, device, units=None, *, out_fill=None):
+    """lsv_attn_fwd_fp8_tail and lsv_attn_fwd_fp8 on the same inputs: (out, lse, ref_out, ref_lse)."""
+    import torch
+    import long_sequence_video_amd as lsv
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in (f8.q, f8.k, f8.v))
+    cu = torch.from_numpy(f8.cu_seqlens.astype(np.int32)).to(device)
+    out = torch.empty(f8.q.shape, dtype=torch.bfloat16, device=device)
+    lse = torch.empty((f8.n_heads, f8.total_tokens), dtype=torch.float32, device=device)
+    if out_fill is not None:
+        out.view(torch.int16).fill_(int(np.int16(np.uint16(out_fill))))
+        lse.fill_(-7.0)
+    lsv.attn_fwd_fp8_tail(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale,
+                          compute_units=units, out=out, lse=lse)
+    ref_o, ref_l = lsv.attn_fwd_fp8(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale)
+    torch.cuda.synchronize(device)
+    return from_dev(out), lse.cpu().numpy(), from_dev(ref_o), ref_l.cpu().numpy()

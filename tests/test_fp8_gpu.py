@@ -238,8 +238,7 @@ def test_fp8_largest_supported_segment(gpu):
     # The tail launch on the same inputs (the device's plan: the last tiles of one head per XCD,
     # so the cut ranges start deep into the segment): whole tiles bit-identical to the plain
     # launch, every row of the cut tiles on the cut heads against the oracle.
-    from tests.gpu_common import whole_tile_rows
-    from tests.test_fp8_tail_gpu import run_fp8_tail
+    from tests.gpu_common import run_fp8_tail, whole_tile_rows
     import long_sequence_video_amd as lsv
     whole, split, n_tail = whole_tile_rows(f8, lsv.lsv_device_peak(0)[1])
     say(f"case fp8 max segment 599186 x 56: tail launch, {n_tail} tail tiles x {split} ranges")

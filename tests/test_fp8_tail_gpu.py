@@ -15,28 +15,10 @@ import numpy as np
 import pytest
 
 from long_sequence_video_amd import inputs as gen
-from tests.gpu_common import from_dev, sample_rows, say, whole_tile_rows
+from tests.gpu_common import run_fp8_tail, sample_rows, say, whole_tile_rows
 from tests.test_fp8_gpu import compare_fp8
 
 pytestmark = pytest.mark.gpu
-
-
-def run_fp8_tail(f8, device, units=None, *, out_fill=None):
-    """lsv_attn_fwd_fp8_tail and lsv_attn_fwd_fp8 on the same inputs: (out, lse, ref_out, ref_lse)."""
-    import torch
-    import long_sequence_video_amd as lsv
-    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in (f8.q, f8.k, f8.v))
-    cu = torch.from_numpy(f8.cu_seqlens.astype(np.int32)).to(device)
-    out = torch.empty(f8.q.shape, dtype=torch.bfloat16, device=device)
-    lse = torch.empty((f8.n_heads, f8.total_tokens), dtype=torch.float32, device=device)
-    if out_fill is not None:
-        out.view(torch.int16).fill_(int(np.int16(np.uint16(out_fill))))
-        lse.fill_(-7.0)
-    lsv.attn_fwd_fp8_tail(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale,
-                          compute_units=units, out=out, lse=lse)
-    ref_o, ref_l = lsv.attn_fwd_fp8(q, k, v, f8.descale_q, f8.descale_k, f8.descale_v, cu, f8.max_seqlen, f8.scale)
-    torch.cuda.synchronize(device)
-    return from_dev(out), lse.cpu().numpy(), from_dev(ref_o), ref_l.cpu().numpy()
 
 
 def check_whole_tiles(out, lse, ref_o, ref_l, whole):
