@@ -25,7 +25,7 @@ Not part of ``value``.
 
 An object ``forward_legs`` times the same forward on each of the other workloads (the
 104,000-token segment of the pack alone, the 40% target row; 4,096 x 56 with boosted keys;
-the sp=4 share 19,394 x 14; 38,000 x 56; the tiny 256 x 4 case), each with its own steps and
+the sp=4 shares 19,394 x 14 and 38,000 x 14; 38,000 x 56; the tiny 256 x 4 case), each with its own steps and
 the same automatic key split as the headline. Not part of ``value``. One more leg,
 ``fallback_s38000_h56``, is 38,000 x 56 with every query's first key tile scoring far below the
 rest, so that every workgroup's fixed-reference pass overflows and reruns on the exact path;
@@ -457,7 +457,8 @@ def time_forward(inp, steps: int, warmup: int, split="auto"):
 
 # The forward legs of the default run: (workload, timed launches) -- about half a second of
 # GPU time each, plus a few warmup launches.
-FORWARD_LEGS = {"h56_s104000": 4, "s4096_h56_kboost": 400, "sp4_share_s19394_h14": 100, "h3_s38000_h56": 20,
+FORWARD_LEGS = {"h56_s104000": 4, "s4096_h56_kboost": 400, "sp4_share_s19394_h14": 100, "sp4_share_s38000_h14": 50,
+                "h3_s38000_h56": 20,
                 "tiny_s256_h4": 400, "fallback_s38000_h56": 8}
 
 
