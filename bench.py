@@ -521,7 +521,34 @@ def cpu_baseline(inp, target_seconds: float = 15.0):
         "sample": (f"{len(rows)} query rows ({per_seg} per segment, all {inp.n_heads} heads) of the same "
                    f"workload against every key of their segment; fp64 numpy oracle, {cores} threads; "
                    f"{f:.3e} flops in {dt:.1f} s"),
+        "cpu_model": host_cpu_model(),
+        "blas": host_blas(),
     }
+
+
+def host_cpu_model() -> str | None:
+    """The host CPU's model name (/proc/cpuinfo), or None where that file has none."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_blas() -> str | None:
+    """numpy's BLAS backend and version. The oracle runs it single-threaded inside each of its
+    worker threads, so the thread count is the `cores` figure."""
+    try:
+        from threadpoolctl import threadpool_info
+    except ImportError:
+        return None
+    libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    if not libs:
+        return None
+    return ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs)
 
 
 def bench_gemm_reference(dtype: str = "bf16", steps: int = 50, warmup: int = 5, n: int = 16384):

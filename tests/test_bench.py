@@ -25,6 +25,10 @@ def test_cpu_baseline_leg_reports_the_oracle_on_host_cores():
     res = bench.cpu_baseline(gen.make_config("tiny_s256_h4"), target_seconds=0.2)
     assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s"
     assert res["value"] > 0 and res["cores"] >= 1 and res["sample"]
+    # the host's CPU model and numpy's BLAS are named beside the rate (null only where the host
+    # does not say)
+    assert "cpu_model" in res and "blas" in res
+    assert res["blas"] is None or "blas" in res["blas"].lower()
 
 
 def test_counter_summary_is_stale_once_a_device_header_changes(tmp_path, monkeypatch):
